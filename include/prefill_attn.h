@@ -1,0 +1,152 @@
+/*
+ * prefill_attn.h -- fused RoPE causal prefill attention for AMD MI355X (gfx950).
+ *
+ * One call computes, for every batch element b, query head h and query token i,
+ *
+ *     O[b,i,h,:] = sum_{j<=i} softmax_j( RoPE(Q[b,i,h,:]) . RoPE(K[b,j,kvh(h),:]) * scale ) V[b,j,kvh(h),:]
+ *
+ * in a single kernel launch: RoPE is applied to Q and K inside the kernel from
+ * cos/sin tables built once at init, the causal Q.K^T is computed tile by tile,
+ * the softmax is evaluated blockwise with a running max and sum, and P.V is
+ * accumulated, so no S x S score matrix is ever written to memory.
+ *
+ * Sources (page title and section):
+ *  - "手写内核实现6倍prefill加速：边缘LLM推理的内存与计算协同优化"
+ *    (www.0539edu.com/news/6082052): §2.2 one kernel fuses RoPE, Q.K^T, mask,
+ *    softmax and the P.V product; §3.1 RoPE as a complex multiply with cos/sin
+ *    tables indexed by position, done inside the Q.K^T loop; §2.2 all memory
+ *    reserved once at start-up, none during a run.
+ *  - the 2kiu.com/news/6082051 retelling of the same engine: §1.2 the three-call
+ *    C interface (init / run / cleanup); §2.1 blocked attention with a constant
+ *    working set and no S x S matrix; §3.3 int16 fixed-point RoPE tables.
+ *  - the MNN-on-K3 blog (zhaode.wang/blog/2026/mnn-k3-riscv), §六: fused
+ *    attention as blocked online softmax.
+ *  - the XNet-DNN article (www.szyisi.cn/article/817147.html), §三.3
+ *    FlashAttention-2: online softmax with the rescale deferred to the end.
+ *
+ * Conventions shared by every call:
+ *  - Every function returns PA_OK (0) or a negative PA_E* code; nothing throws
+ *    across this interface.
+ *  - Tensors are dense row-major: Q [batch][seq_len][n_heads][head_dim],
+ *    K and V [batch][seq_len][n_kv_heads][head_dim], O [batch][seq_len][n_heads][head_dim].
+ *  - Query head h reads KV head kvh(h) = h / (n_heads / n_kv_heads) (contiguous
+ *    groups, the repeat-interleave convention for grouped-query attention).
+ *  - RoPE rotates adjacent pairs (x, y) = (X[2k], X[2k+1]) by the angle
+ *    p * theta_k, theta_k = rope_theta^(-2k/head_dim), where p = pos_offsets[b] + i
+ *    is the position of token i of batch element b (queries and keys alike; the
+ *    causal mask stays j <= i).
+ *  - Device pointers must belong to the device that was current at init and be
+ *    16-byte aligned.  The caller owns Q, K, V, O, pos_offsets and the stream;
+ *    the handle owns its device tables and its status word.
+ */
+#ifndef PREFILL_ATTN_H
+#define PREFILL_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct prefill_attn prefill_attn; /* opaque handle */
+
+/* Input element types accepted by prefill_attn_run. */
+enum prefill_attn_dtype {
+    PA_IN_F32 = 0,  /* Q, K, V float32; products on the fp32 matrix cores */
+    PA_IN_BF16 = 1, /* Q, K, V bfloat16; rotated Q'/K', P and V rounded to fp16 for the matrix cores, fp32 accumulate */
+    PA_IN_I16 = 2   /* Q, K int16 fixed point, V bfloat16; integer RoPE, exact int32 scores, fp32 softmax */
+};
+
+enum prefill_attn_status {
+    PA_OK = 0,
+    PA_EINVAL = -1,  /* bad argument: shape, NULL or misaligned pointer, unknown dtype */
+    PA_ENOMEM = -2,  /* device or host allocation failed (init only) */
+    PA_EDEVICE = -3, /* no device, or the current device is not gfx950 */
+    PA_ELAUNCH = -4, /* the HIP runtime rejected a launch or a copy */
+    PA_ERANGE = -5   /* a run saw pos_offsets[b] < 0 or pos_offsets[b] + seq_len > max_seq */
+};
+
+/*
+ * Create a handle for one attention shape on the current HIP device.
+ *   n_heads     query heads, >= 1
+ *   n_kv_heads  key/value heads, >= 1, dividing n_heads
+ *   head_dim    64, 96 or 128
+ *   max_seq     largest position + 1 any run may use (table rows), 1 .. 1048576
+ *   rope_theta  RoPE base, > 1
+ * Builds the RoPE cos/sin tables on the host in fp64 (rounded once to fp32 pairs
+ * and to Q1.14 int16 pairs), copies them to the device and allocates the status
+ * word.  All allocation happens here; prefill_attn_run allocates nothing.
+ * On success *out receives the handle; on failure *out is set to NULL.
+ */
+int prefill_attn_init(prefill_attn** out, int n_heads, int n_kv_heads, int head_dim,
+                      int max_seq, double rope_theta);
+
+/*
+ * Enqueue one fused attention pass on `stream` (a hipStream_t; NULL = the null
+ * stream).  Asynchronous: returns once the kernel is queued; no host sync, no
+ * allocation.
+ *   in_dtype     a prefill_attn_dtype value
+ *   batch        >= 0; seq_len in 0 .. max_seq (batch == 0 or seq_len == 0 is a no-op)
+ *   q, k, v      device tensors in the layouts above, of in_dtype (V is bf16 for PA_IN_I16)
+ *   pos_offsets  device int32[batch], or NULL for all zeros
+ *   out          device float32 O; every element of rows i < seq_len is written
+ *   score_scale  multiplies the score: PA_IN_F32/PA_IN_BF16 logit = (Q'.K') * score_scale,
+ *                PA_IN_I16 logit = (int32 score) * score_scale; 0 selects 1/sqrt(head_dim)
+ * A batch element whose positions leave [0, max_seq) gets O = 0 and sets the
+ * handle's status word (read it with prefill_attn_status).  Runs on one handle
+ * may overlap on several streams; they share only that status word.
+ */
+int prefill_attn_run(const prefill_attn* h, int in_dtype, int batch, int seq_len,
+                     const void* q, const void* k, const void* v,
+                     const int32_t* pos_offsets, float* out, float score_scale,
+                     void* stream);
+
+/*
+ * Synchronise `stream`, then report and clear the status word: PA_ERANGE if any
+ * run since the last call saw an out-of-range position, else PA_OK.
+ */
+int prefill_attn_status(prefill_attn* h, void* stream);
+
+/* Free everything init allocated.  NULL-safe.  Synchronises the device first. */
+int prefill_attn_destroy(prefill_attn* h);
+
+/* Static English text for a status code. */
+const char* prefill_attn_strerror(int code);
+
+/*
+ * Host-only RoPE table builders (no device needed), the same code init uses.
+ * Row p, pair k of the result holds the angle a = p * rope_theta^(-2k/head_dim),
+ * evaluated in fp64:
+ *   _f32: out[(p*head_dim/2 + k)*2 + 0] = (float)cos(a), [... + 1] = (float)sin(a)
+ *         (round to nearest even), out has max_seq*head_dim floats;
+ *   _q14: out[(p*head_dim/2 + k)*2 + 0] = round(cos(a) * 2^14), [... + 1] = round(sin(a) * 2^14)
+ *         (nearest, ties away from zero), out has max_seq*head_dim int16.
+ * head_dim must be even and positive, max_seq positive; out is caller-owned host memory.
+ */
+int prefill_attn_rope_table_f32(int max_seq, int head_dim, double rope_theta, float* out);
+int prefill_attn_rope_table_q14(int max_seq, int head_dim, double rope_theta, int16_t* out);
+
+/*
+ * Test exports for the int16 variant: the same device code as PA_IN_I16 runs,
+ * with an epilogue that writes intermediate results instead of O.
+ *   prefill_attn_debug_rope_i16: x [batch][seq_len][n_heads_x][head_dim] int16 ->
+ *     x_rot (same shape) = (x C - y S + 2^13) >> 14, (x S + y C + 2^13) >> 14 at
+ *     position pos_offsets[b] + i (the fixed-point rotation of the page titled
+ *     "手写内核实现6倍prefill加速", §3.1, with Q1.14 tables).
+ *   prefill_attn_debug_scores_i32: the full (unmasked) int32 score matrix
+ *     scores[batch][n_heads][seq_len][seq_len], scores[b][h][i][j] = Q'[b,i,h] . K'[b,j,kvh(h)],
+ *     computed by the int8 digit-split matrix-core path of PA_IN_I16.
+ * Same pointer, alignment and stream rules as prefill_attn_run.
+ */
+int prefill_attn_debug_rope_i16(const prefill_attn* h, int batch, int seq_len,
+                                const int16_t* x, int n_heads_x, const int32_t* pos_offsets,
+                                int16_t* x_rot, void* stream);
+int prefill_attn_debug_scores_i32(const prefill_attn* h, int batch, int seq_len,
+                                  const int16_t* q, const int16_t* k, const int32_t* pos_offsets,
+                                  int32_t* scores, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PREFILL_ATTN_H */

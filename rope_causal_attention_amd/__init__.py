@@ -1,0 +1,243 @@
+"""Python binding of libprefill_attn.so: fused RoPE causal prefill attention.
+
+Argument marshalling only: every step of the attention runs in the HIP kernels
+of the C-ABI library (``include/prefill_attn.h``).  PyTorch supplies device
+memory and the stream.  There is no other implementation behind these names:
+if the library is missing or cannot be loaded, every call raises.
+
+torch is imported before the library is loaded so that the library's
+``libamdhip64.so.7`` dependency resolves to the HIP runtime torch already has
+in the process (one runtime, so torch's streams and pointers are valid in the
+library); :func:`load_library` checks that only one HIP runtime is mapped.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "PA_IN_F32", "PA_IN_BF16", "PA_IN_I16",
+    "PA_OK", "PA_EINVAL", "PA_ENOMEM", "PA_EDEVICE", "PA_ELAUNCH", "PA_ERANGE",
+    "PrefillAttnError", "load_library", "library_path",
+    "prefill_attn_init", "prefill_attn_run", "prefill_attn_status", "prefill_attn_destroy",
+    "prefill_attn_strerror", "prefill_attn_rope_table_f32", "prefill_attn_rope_table_q14",
+    "prefill_attn_debug_rope_i16", "prefill_attn_debug_scores_i32",
+    "PrefillAttention", "EXPORTED_SYMBOLS",
+]
+
+PA_IN_F32, PA_IN_BF16, PA_IN_I16 = 0, 1, 2
+PA_OK, PA_EINVAL, PA_ENOMEM, PA_EDEVICE, PA_ELAUNCH, PA_ERANGE = 0, -1, -2, -3, -4, -5
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libprefill_attn.so")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGNATURES = {
+    "prefill_attn_init": (_I, [ctypes.POINTER(_P), _I, _I, _I, _I, ctypes.c_double]),
+    "prefill_attn_run": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_float, _P]),
+    "prefill_attn_status": (_I, [_P, _P]),
+    "prefill_attn_destroy": (_I, [_P]),
+    "prefill_attn_strerror": (ctypes.c_char_p, [_I]),
+    "prefill_attn_rope_table_f32": (_I, [_I, _I, ctypes.c_double, _P]),
+    "prefill_attn_rope_table_q14": (_I, [_I, _I, ctypes.c_double, _P]),
+    "prefill_attn_debug_rope_i16": (_I, [_P, _I, _I, _P, _I, _P, _P, _P]),
+    "prefill_attn_debug_scores_i32": (_I, [_P, _I, _I, _P, _P, _P, _P, _P]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class PrefillAttnError(RuntimeError):
+    def __init__(self, code, what):
+        self.code = code
+        super().__init__(f"{what}: {_strerror(code)} ({code})")
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _hip_runtimes_mapped():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def load_library():
+    """Load (once) and return the ctypes handle of libprefill_attn.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m rope_causal_attention_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"more than one HIP runtime is mapped into the process: {sorted(runtimes)}")
+    _lib = lib
+    return lib
+
+
+def _strerror(code):
+    try:
+        return load_library().prefill_attn_strerror(int(code)).decode()
+    except Exception:  # noqa: BLE001 - only used while formatting an error
+        return "unknown status code"
+
+
+def _check(code, what):
+    if code != PA_OK:
+        raise PrefillAttnError(code, what)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+# ------------------------------------------------------------------ C calls
+
+def prefill_attn_init(n_heads, n_kv_heads, head_dim, max_seq, rope_theta):
+    """Create a handle on the current device (see prefill_attn_init in the header)."""
+    h = _P()
+    _check(load_library().prefill_attn_init(ctypes.byref(h), n_heads, n_kv_heads, head_dim, max_seq,
+                                            float(rope_theta)), "prefill_attn_init")
+    return h.value
+
+
+def prefill_attn_run(handle, in_dtype, batch, seq_len, q, k, v, pos_offsets, out, score_scale=0.0,
+                     stream=None):
+    """Enqueue one fused attention pass; tensors or raw device pointers."""
+    _check(load_library().prefill_attn_run(handle, in_dtype, batch, seq_len, _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(pos_offsets), _ptr(out), float(score_scale), _stream(stream)),
+           "prefill_attn_run")
+
+
+def prefill_attn_status(handle, stream=None):
+    """Synchronise the stream; return PA_OK or PA_ERANGE (and clear the flag)."""
+    code = load_library().prefill_attn_status(handle, _stream(stream))
+    if code not in (PA_OK, PA_ERANGE):
+        raise PrefillAttnError(code, "prefill_attn_status")
+    return code
+
+
+def prefill_attn_destroy(handle):
+    _check(load_library().prefill_attn_destroy(handle), "prefill_attn_destroy")
+
+
+def prefill_attn_strerror(code):
+    return _strerror(code)
+
+
+def prefill_attn_rope_table_f32(max_seq, head_dim, rope_theta):
+    """Host table [max_seq][head_dim/2][2] float32 (cos, sin)."""
+    out = np.empty((max_seq, head_dim // 2, 2), dtype=np.float32)
+    _check(load_library().prefill_attn_rope_table_f32(max_seq, head_dim, float(rope_theta),
+                                                      out.ctypes.data), "prefill_attn_rope_table_f32")
+    return out
+
+
+def prefill_attn_rope_table_q14(max_seq, head_dim, rope_theta):
+    """Host table [max_seq][head_dim/2][2] int16 (C, S) in Q1.14."""
+    out = np.empty((max_seq, head_dim // 2, 2), dtype=np.int16)
+    _check(load_library().prefill_attn_rope_table_q14(max_seq, head_dim, float(rope_theta),
+                                                      out.ctypes.data), "prefill_attn_rope_table_q14")
+    return out
+
+
+def prefill_attn_debug_rope_i16(handle, batch, seq_len, x, n_heads_x, pos_offsets, x_rot, stream=None):
+    _check(load_library().prefill_attn_debug_rope_i16(handle, batch, seq_len, _ptr(x), n_heads_x,
+                                                      _ptr(pos_offsets), _ptr(x_rot), _stream(stream)),
+           "prefill_attn_debug_rope_i16")
+
+
+def prefill_attn_debug_scores_i32(handle, batch, seq_len, q, k, pos_offsets, scores, stream=None):
+    _check(load_library().prefill_attn_debug_scores_i32(handle, batch, seq_len, _ptr(q), _ptr(k),
+                                                        _ptr(pos_offsets), _ptr(scores), _stream(stream)),
+           "prefill_attn_debug_scores_i32")
+
+
+# ------------------------------------------------------------- tensor helper
+
+_DTYPES = {torch.float32: PA_IN_F32, torch.bfloat16: PA_IN_BF16, torch.int16: PA_IN_I16}
+
+
+class PrefillAttention:
+    """A handle plus tensor marshalling: ``attn(q, k, v) -> O`` (float32).
+
+    q [B][S][Hq][D], k/v [B][S][Hkv][D] on the handle's device, contiguous;
+    float32 or bfloat16 Q/K/V, or int16 Q/K with bfloat16 V.
+    """
+
+    def __init__(self, n_heads, n_kv_heads, head_dim, max_seq, rope_theta=10000.0):
+        self.n_heads, self.n_kv_heads, self.head_dim = n_heads, n_kv_heads, head_dim
+        self.max_seq, self.rope_theta = max_seq, rope_theta
+        self.handle = prefill_attn_init(n_heads, n_kv_heads, head_dim, max_seq, rope_theta)
+
+    def close(self):
+        if self.handle:
+            prefill_attn_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+    def _validate(self, q, k, v, pos_offsets, out):
+        if q.dtype not in _DTYPES:
+            raise TypeError(f"unsupported q dtype {q.dtype}")
+        dt = _DTYPES[q.dtype]
+        want_kv = q.dtype
+        if k.dtype != want_kv or v.dtype != (torch.bfloat16 if dt == PA_IN_I16 else want_kv):
+            raise TypeError("k must match q's dtype; v must too (bfloat16 for int16 q/k)")
+        B, S, Hq, D = q.shape
+        if Hq != self.n_heads or D != self.head_dim:
+            raise ValueError("q shape does not match the handle")
+        if tuple(k.shape) != (B, S, self.n_kv_heads, D) or tuple(v.shape) != (B, S, self.n_kv_heads, D):
+            raise ValueError("k/v shape must be [B][S][n_kv_heads][head_dim]")
+        for t in (q, k, v) + ((out,) if out is not None else ()):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("tensors must be contiguous device tensors")
+        if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (B, S, Hq, D)):
+            raise ValueError("out must be float32 [B][S][n_heads][head_dim]")
+        if pos_offsets is not None and (pos_offsets.dtype != torch.int32 or pos_offsets.numel() != B
+                                        or not pos_offsets.is_cuda):
+            raise ValueError("pos_offsets must be a device int32 tensor with one entry per batch element")
+        return dt, B, S
+
+    def __call__(self, q, k, v, pos_offsets=None, score_scale=0.0, out=None, stream=None):
+        dt, B, S = self._validate(q, k, v, pos_offsets, out)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        prefill_attn_run(self.handle, dt, B, S, q, k, v, pos_offsets, out, score_scale, stream)
+        return out
+
+    def status(self, stream=None):
+        return prefill_attn_status(self.handle, stream)

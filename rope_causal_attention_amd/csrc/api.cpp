@@ -1,0 +1,197 @@
+// C-ABI of the fused RoPE causal prefill attention library.
+//
+// The three-call shape (init binds the constant data and reserves memory once,
+// run computes, cleanup releases) follows the interface of the 2kiu.com
+// retelling of the hand-written prefill engine (§1.2); the "no allocation after
+// start-up" rule is the page titled "手写内核实现6倍prefill加速" (§2.2).  Unlike
+// those pages' interface this one reports every failure as a status code.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "internal.h"
+#include "prefill_attn.h"
+
+struct prefill_attn {
+    int device;
+    int n_heads;
+    int n_kv_heads;
+    int head_dim;
+    int max_seq;
+    double rope_theta;
+    float* d_rope_f32;
+    int16_t* d_rope_q14;
+    int* d_status;
+};
+
+namespace {
+
+constexpr int kMaxSeq = 1 << 20;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+void free_handle(prefill_attn* h) {
+    if (!h) return;
+    if (h->d_rope_f32) (void)hipFree(h->d_rope_f32);
+    if (h->d_rope_q14) (void)hipFree(h->d_rope_q14);
+    if (h->d_status) (void)hipFree(h->d_status);
+    delete h;
+}
+
+// Checks shared by run and the test exports; fills the common launch arguments.
+int prepare(const prefill_attn* h, int batch, int seq_len, const int32_t* pos_offsets, pa::RunArgs& a) {
+    if (!h || batch < 0 || seq_len < 0 || seq_len > h->max_seq) return PA_EINVAL;
+    if (pos_offsets && !aligned4(pos_offsets)) return PA_EINVAL;
+    // every index the kernels form stays below 2^62; the grid below 2^31 workgroups
+    const long long qblocks = (static_cast<long long>(seq_len) + 127) / 128;
+    if (qblocks * batch * h->n_heads > 0x7fffffffLL) return PA_EINVAL;
+    std::memset(&a, 0, sizeof(a));
+    a.pos_offsets = pos_offsets;
+    a.rope_f32 = h->d_rope_f32;
+    a.rope_q14 = h->d_rope_q14;
+    a.status = h->d_status;
+    a.batch = batch;
+    a.seq_len = seq_len;
+    a.n_heads = h->n_heads;
+    a.n_kv_heads = h->n_kv_heads;
+    a.max_seq = h->max_seq;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int prefill_attn_init(prefill_attn** out, int n_heads, int n_kv_heads, int head_dim, int max_seq,
+                                 double rope_theta) {
+    if (!out) return PA_EINVAL;
+    *out = nullptr;
+    if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads != 0) return PA_EINVAL;
+    if (head_dim != 64 && head_dim != 96 && head_dim != 128) return PA_EINVAL;
+    if (max_seq < 1 || max_seq > kMaxSeq) return PA_EINVAL;
+    if (!std::isfinite(rope_theta) || rope_theta <= 1.0) return PA_EINVAL;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_EDEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PA_EDEVICE;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return PA_EDEVICE;
+
+    const size_t n = static_cast<size_t>(max_seq) * head_dim;  // (cos, sin) pairs x D/2 per row
+    std::vector<float> t32;
+    std::vector<int16_t> t14;
+    try {
+        t32.resize(n);
+        t14.resize(n);
+    } catch (const std::bad_alloc&) {
+        return PA_ENOMEM;
+    }
+    if (prefill_attn_rope_table_f32(max_seq, head_dim, rope_theta, t32.data()) != PA_OK ||
+        prefill_attn_rope_table_q14(max_seq, head_dim, rope_theta, t14.data()) != PA_OK)
+        return PA_EINVAL;
+
+    prefill_attn* h = new (std::nothrow) prefill_attn{dev, n_heads, n_kv_heads, head_dim, max_seq, rope_theta,
+                                                      nullptr, nullptr, nullptr};
+    if (!h) return PA_ENOMEM;
+    if (hipMalloc(&h->d_rope_f32, n * sizeof(float)) != hipSuccess ||
+        hipMalloc(&h->d_rope_q14, n * sizeof(int16_t)) != hipSuccess ||
+        hipMalloc(&h->d_status, sizeof(int)) != hipSuccess) {
+        free_handle(h);
+        return PA_ENOMEM;
+    }
+    if (hipMemcpy(h->d_rope_f32, t32.data(), n * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(h->d_rope_q14, t14.data(), n * sizeof(int16_t), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemset(h->d_status, 0, sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        free_handle(h);
+        return PA_ELAUNCH;
+    }
+    *out = h;
+    return PA_OK;
+}
+
+extern "C" int prefill_attn_run(const prefill_attn* h, int in_dtype, int batch, int seq_len, const void* q,
+                                const void* k, const void* v, const int32_t* pos_offsets, float* out,
+                                float score_scale, void* stream) {
+    pa::RunArgs a;
+    const int rc = prepare(h, batch, seq_len, pos_offsets, a);
+    if (rc != PA_OK) return rc;
+    if (in_dtype != PA_IN_F32 && in_dtype != PA_IN_BF16 && in_dtype != PA_IN_I16) return PA_EINVAL;
+    if (!std::isfinite(score_scale)) return PA_EINVAL;
+    if (batch == 0 || seq_len == 0) return PA_OK;
+    if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return PA_EINVAL;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.score_scale = score_scale != 0.0f ? score_scale : 1.0f / std::sqrt(static_cast<float>(h->head_dim));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (in_dtype) {
+        case PA_IN_F32: e = pa::launch_attn_f32(h->head_dim, a, s); break;
+        case PA_IN_BF16: e = pa::launch_attn_bf16(h->head_dim, a, s); break;
+        default: e = pa::launch_attn_i16(h->head_dim, a, s); break;
+    }
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+extern "C" int prefill_attn_status(prefill_attn* h, void* stream) {
+    if (!h) return PA_EINVAL;
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ELAUNCH;
+    int flag = 0;
+    if (hipMemcpy(&flag, h->d_status, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return PA_ELAUNCH;
+    if (flag != 0 && hipMemset(h->d_status, 0, sizeof(int)) != hipSuccess) return PA_ELAUNCH;
+    if (hipDeviceSynchronize() != hipSuccess) return PA_ELAUNCH;
+    return flag ? PA_ERANGE : PA_OK;
+}
+
+extern "C" int prefill_attn_destroy(prefill_attn* h) {
+    if (!h) return PA_OK;
+    const bool ok = hipDeviceSynchronize() == hipSuccess;
+    free_handle(h);
+    return ok ? PA_OK : PA_ELAUNCH;
+}
+
+extern "C" const char* prefill_attn_strerror(int code) {
+    switch (code) {
+        case PA_OK: return "success";
+        case PA_EINVAL: return "invalid argument";
+        case PA_ENOMEM: return "out of memory";
+        case PA_EDEVICE: return "no usable gfx950 device";
+        case PA_ELAUNCH: return "HIP runtime error";
+        case PA_ERANGE: return "position outside the RoPE table";
+        default: return "unknown status code";
+    }
+}
+
+extern "C" int prefill_attn_debug_rope_i16(const prefill_attn* h, int batch, int seq_len, const int16_t* x,
+                                           int n_heads_x, const int32_t* pos_offsets, int16_t* x_rot,
+                                           void* stream) {
+    pa::RunArgs a;
+    const int rc = prepare(h, batch, seq_len, pos_offsets, a);
+    if (rc != PA_OK) return rc;
+    if (n_heads_x < 1) return PA_EINVAL;
+    if (batch == 0 || seq_len == 0) return PA_OK;
+    if (!x || !x_rot || !aligned16(x) || !aligned16(x_rot)) return PA_EINVAL;
+    a.q = x;
+    hipError_t e = pa::launch_debug_rope_i16(h->head_dim, a, n_heads_x, x_rot, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+extern "C" int prefill_attn_debug_scores_i32(const prefill_attn* h, int batch, int seq_len, const int16_t* q,
+                                             const int16_t* k, const int32_t* pos_offsets, int32_t* scores,
+                                             void* stream) {
+    pa::RunArgs a;
+    const int rc = prepare(h, batch, seq_len, pos_offsets, a);
+    if (rc != PA_OK) return rc;
+    if (batch == 0 || seq_len == 0) return PA_OK;
+    if (!q || !k || !scores || !aligned16(q) || !aligned16(k) || !aligned16(scores)) return PA_EINVAL;
+    a.q = q;
+    a.k = k;
+    hipError_t e = pa::launch_debug_scores_i32(h->head_dim, a, scores, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}

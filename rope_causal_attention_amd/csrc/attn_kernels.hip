@@ -1,0 +1,807 @@
+// Fused RoPE causal prefill attention kernels for gfx950 (MI355X).
+//
+// What is computed (pages cited by title and section):
+//  * "手写内核实现6倍prefill加速：边缘LLM推理的内存与计算协同优化", §2.2/§3.1:
+//    one kernel applies RoPE to Q and K from position-indexed cos/sin tables
+//    (a complex multiply on adjacent pairs), forms Q.K^T, applies the mask,
+//    the softmax and the product with V; rotated K goes straight into the dot
+//    product and is never written back to memory.
+//  * 2kiu.com/news/6082051 retelling, §2.1: attention in blocks of Q rows and
+//    K columns with a working set independent of the sequence length; §3.3:
+//    int16 fixed-point RoPE tables and activations.
+//  * MNN-on-K3 blog (zhaode.wang/blog/2026/mnn-k3-riscv), §六: QK, online
+//    softmax and PV merged into one blocked pass; §三: an 8-bit operand split
+//    into two narrower digits whose products recombine exactly.
+//  * XNet-DNN article (www.szyisi.cn/article/817147.html), §三.3
+//    FlashAttention-2: Q in the outer loop so work spreads over sequence
+//    blocks, Q rows split across waves that share the K/V tiles, the rescale
+//    by the running sum deferred to the end.
+//
+// gfx950 design (not a translation of the pages' CPU/NPU code):
+//  * one workgroup = 4 waves x 32 query rows (BM = 128) of one (batch, head);
+//    K/V tiles of 64 keys are staged in LDS, double-buffered, so the global
+//    loads of tile t+1 are in flight while tile t is on the matrix cores;
+//  * S^T = K'.Q'^T on v_mfma_f32_32x32x16_f16: each lane then owns one query
+//    column and 16 keys of every 32x32 block, so the softmax row max / row sum
+//    are in-lane plus one v_permlane32_swap between the two lane halves;
+//  * the f16 probabilities stay in registers and feed O^T += V^T.P^T directly
+//    as the B operand; V^T is written to LDS transposed (and with the key order
+//    the accumulator layout implies) while V is converted bf16 -> f16;
+//  * Q' is rotated once per workgroup, pre-multiplied by score_scale*log2(e)
+//    and kept in registers for the whole key loop; exp2 replaces exp;
+//  * the running max is only moved (and O, l rescaled) when it grows by more
+//    than 2^8, which keeps the result exact (the same stale max is used for O
+//    and for l) and skips almost every rescale;
+//  * workgroups are ordered longest (most keys) first, and the (batch, head)
+//    pairs are split over the 8 XCDs so one head's K/V stays in one L2.
+//  * int16 variant: Q'/K' rotated in integers, split into signed 8-bit digits
+//    a = 128 h + l (l in [-64, 63], h in [-23, 23] for |a| <= 2897), and the
+//    exact int32 score is recombined from three v_mfma_i32_32x32x32_i8
+//    products (hh, ll and (h+l)(h+l)); P.V as in the bf16 kernel.
+//  * fp32 variant: v_mfma_f32_32x32x2_f32 for both products, fp32 LDS tiles.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int BM = 32 * kWaves;  // query rows per workgroup
+constexpr int BN = 64;           // keys per LDS tile
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8 between rescales
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ int i16_lo(uint32_t w) { return static_cast<int>(w << 16) >> 16; }
+__device__ __forceinline__ int i16_hi(uint32_t w) { return static_cast<int>(w) >> 16; }
+
+// Two fp32 -> packed fp16, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    f16x2 h = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Combine a per-lane value with the same lane of the other 32-lane half.
+__device__ __forceinline__ float halves_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row index of accumulator element v (0..15) of a 32x32 MFMA result for lane
+// half lh: rows come in groups of 4, interleaved between the two halves.
+__device__ __forceinline__ int acc_row(int v, int lh) { return 8 * (v >> 2) + 4 * lh + (v & 3); }
+
+// Work order: longest query blocks first; when the (batch, head) count is a
+// multiple of 8, consecutive workgroup ids (dealt round-robin to the 8 XCDs)
+// are mapped so that each XCD owns a contiguous range of (batch, head).
+struct BlockPos {
+    int qb, b, hq;
+};
+__device__ __forceinline__ BlockPos map_block(int n_qblocks, int batch, int n_heads) {
+    const int BH = batch * n_heads;
+    const int bid = blockIdx.x;
+    int qb, bh;
+    if ((BH & 7) == 0) {
+        const int x = bid & 7, j = bid >> 3, hpx = BH >> 3;
+        qb = n_qblocks - 1 - j / hpx;
+        bh = x * hpx + j % hpx;
+    } else {
+        qb = n_qblocks - 1 - bid / BH;
+        bh = bid % BH;
+    }
+    return {qb, bh / n_heads, bh % n_heads};
+}
+
+struct Ctx {
+    int b, hq, hkv, off, S, q0;
+};
+
+__device__ __forceinline__ bool make_ctx(const RunArgs& a, Ctx& c) {
+    const int n_qblocks = (a.seq_len + BM - 1) / BM;
+    const BlockPos bp = map_block(n_qblocks, a.batch, a.n_heads);
+    c.b = bp.b;
+    c.hq = bp.hq;
+    c.hkv = bp.hq / (a.n_heads / a.n_kv_heads);
+    c.S = a.seq_len;
+    c.q0 = bp.qb * BM;
+    c.off = a.pos_offsets ? a.pos_offsets[bp.b] : 0;
+    return c.off >= 0 && static_cast<long long>(c.off) + a.seq_len <= a.max_seq;
+}
+
+__device__ __forceinline__ size_t q_index(const RunArgs& a, const Ctx& c, int i, int D) {
+    return ((static_cast<size_t>(c.b) * c.S + i) * a.n_heads + c.hq) * D;
+}
+__device__ __forceinline__ size_t kv_index(const RunArgs& a, const Ctx& c, int j, int D) {
+    return ((static_cast<size_t>(c.b) * c.S + j) * a.n_kv_heads + c.hkv) * D;
+}
+
+// A batch element whose positions leave the tables: O = 0 and the status word is set.
+template <int D>
+__device__ void zero_rows(const RunArgs& a, const Ctx& c) {
+    const int rows = min(BM, c.S - c.q0);
+    for (int idx = threadIdx.x; idx < rows * (D / 4); idx += kThreads) {
+        const int r = idx / (D / 4), col = idx % (D / 4);
+        float4* dst = reinterpret_cast<float4*>(a.out + q_index(a, c, c.q0 + r, D)) + col;
+        *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (threadIdx.x == 0) atomicOr(a.status, 1);
+}
+
+// ------------------------------------------------ V tile: bf16 -> f16, transposed
+
+// LDS holds V^T [D][BN + 8] f16.  Thread (kq, dc) reads keys 4kq..4kq+3 at
+// dims 8dc..8dc+7; converting two keys at a time yields (key, key+1) pairs of
+// one dim, i.e. the transpose for free.  Key quads are stored in the order
+// 0,2,1,3 within each 16-key group so that the 8 keys one lane half feeds to
+// a 16-deep MFMA step are contiguous (16-byte LDS reads).
+template <int D>
+struct VStage {
+    static constexpr int kStride = BN + 8;  // f16 per V^T row
+    static constexpr int kBytes = D * kStride * 2;
+    struct Regs {
+        uint4 raw[4];
+    };
+    __device__ static __forceinline__ void load(const RunArgs& a, const Ctx& c, int tile, Regs& r) {
+        const int tid = threadIdx.x;
+        if (tid >= 2 * D) return;
+        const int kq = tid & 15, dc = tid >> 4;
+        const uint16_t* v = static_cast<const uint16_t*>(a.v);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int key = tile * BN + 4 * kq + rr;
+            r.raw[rr] = key < c.S ? *reinterpret_cast<const uint4*>(v + kv_index(a, c, key, D) + 8 * dc)
+                                  : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ static __forceinline__ uint32_t word(const uint4& u, int i) {
+        return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+    }
+    __device__ static __forceinline__ void commit(const Regs& r, _Float16* lds) {
+        const int tid = threadIdx.x;
+        if (tid >= 2 * D) return;
+        const int kq = tid & 15, dc = tid >> 4;
+        const int pos = (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const uint32_t w = word(r.raw[rr], e >> 1);
+                x[rr] = (e & 1) ? bf_hi(w) : bf_lo(w);
+            }
+            uint2 pk = make_uint2(pack_h2(x[0], x[1]), pack_h2(x[2], x[3]));
+            *reinterpret_cast<uint2*>(lds + (8 * dc + e) * kStride + 4 * pos) = pk;
+        }
+    }
+    // O^T[db] += V^T[32db.., 16kk..] . P^T for the 16-key step kk (0..3) of the tile.
+    __device__ static __forceinline__ void pv(const _Float16* lds, int kk, const f16x8& p, f32x16* o, int lq,
+                                              int lh) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const f16x8 a = *reinterpret_cast<const f16x8*>(lds + (32 * db + lq) * kStride + 16 * kk + 8 * lh);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, p, o[db], 0, 0, 0);
+        }
+    }
+};
+
+// ------------------------------------------------ Q.K^T policy: bf16 inputs
+
+template <int D>
+struct Bf16QK {
+    static constexpr int kStride = D + 8;  // f16 per K' row (16-byte pad against bank conflicts)
+    static constexpr int kBytes = BN * kStride * 2;
+    struct Q {
+        f16x8 f[D / 16];
+    };
+    struct KRegs {
+        uint4 raw[D / 32];
+        float4 cs[D / 32][2];
+    };
+
+    // Rotate 4 adjacent pairs: x' = x c - y s, y' = x s + y c; times `scale`.
+    __device__ static __forceinline__ uint4 rotate8(const uint4& raw, const float4& c0, const float4& c1,
+                                                    float scale) {
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float x = bf_lo(w[j]), y = bf_hi(w[j]);
+            const float c = cs[2 * j], s = cs[2 * j + 1];
+            const float xr = fmaf(x, c, -y * s), yr = fmaf(x, s, y * c);
+            o[j] = pack_h2(xr * scale, yr * scale);
+        }
+        return make_uint4(o[0], o[1], o[2], o[3]);
+    }
+
+    __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
+        const int lh = (threadIdx.x & 63) >> 5;
+        const bool ok = qi < c.S;
+        const uint16_t* src = static_cast<const uint16_t*>(a.q) + (ok ? q_index(a, c, qi, D) : 0);
+        const float* tab = a.rope_f32 + static_cast<size_t>(ok ? c.off + qi : 0) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const int d0 = 16 * ks + 8 * lh;
+            uint4 raw = make_uint4(0, 0, 0, 0);
+            float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0;
+            if (ok) {
+                raw = *reinterpret_cast<const uint4*>(src + d0);
+                c0 = *reinterpret_cast<const float4*>(tab + d0);
+                c1 = *reinterpret_cast<const float4*>(tab + d0 + 4);
+            }
+            q.f[ks] = __builtin_bit_cast(f16x8, rotate8(raw, c0, c1, scale));
+        }
+    }
+
+    __device__ static __forceinline__ void load_k(const RunArgs& a, const Ctx& c, int tile, KRegs& r) {
+        const uint16_t* k = static_cast<const uint16_t*>(a.k);
+#pragma unroll
+        for (int it = 0; it < D / 32; ++it) {
+            const int idx = threadIdx.x + kThreads * it;
+            const int row = idx / (D / 8), ch = idx % (D / 8);
+            const int key = tile * BN + row;
+            if (key < c.S) {
+                r.raw[it] = *reinterpret_cast<const uint4*>(k + kv_index(a, c, key, D) + 8 * ch);
+                const float* tab = a.rope_f32 + static_cast<size_t>(c.off + key) * D + 8 * ch;
+                r.cs[it][0] = *reinterpret_cast<const float4*>(tab);
+                r.cs[it][1] = *reinterpret_cast<const float4*>(tab + 4);
+            } else {
+                r.raw[it] = make_uint4(0, 0, 0, 0);
+                r.cs[it][0] = r.cs[it][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+    }
+
+    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
+        _Float16* kl = reinterpret_cast<_Float16*>(lds);
+#pragma unroll
+        for (int it = 0; it < D / 32; ++it) {
+            const int idx = threadIdx.x + kThreads * it;
+            const int row = idx / (D / 8), ch = idx % (D / 8);
+            *reinterpret_cast<uint4*>(kl + row * kStride + 8 * ch) = rotate8(r.raw[it], r.cs[it][0], r.cs[it][1], 1.0f);
+        }
+    }
+
+    // Logits (log2 units) S^T for key block kb (32 keys) of the tile x this wave's 32 queries.
+    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float (&s)[16], int lq, int lh) {
+        const _Float16* row = reinterpret_cast<const _Float16*>(lds) + (32 * kb + lq) * kStride + 8 * lh;
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const f16x8 a = *reinterpret_cast<const f16x8*>(row + 16 * ks);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, q.f[ks], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = acc[v];
+    }
+};
+
+// ------------------------------------------------ Q.K^T policy: int16 inputs
+
+template <int D>
+struct I16QK {
+    static constexpr int kRow = D + 16;  // bytes per 8-bit digit row
+    static constexpr int kPlane = BN * kRow;
+    static constexpr int kBytes = 3 * kPlane;  // planes: high digit, low digit, high + low
+    struct Q {
+        i32x4 h[D / 32], l[D / 32], m[D / 32];
+        float scale;
+    };
+    struct KRegs {
+        uint4 raw[D / 32];
+        uint4 cs[D / 32];
+    };
+
+    // Fixed-point rotation with round-half-up: (x C - y S + 2^13) >> 14, (x S + y C + 2^13) >> 14.
+    __device__ static __forceinline__ int rot_x(int x, int y, int C, int S) { return (x * C - y * S + 8192) >> 14; }
+    __device__ static __forceinline__ int rot_y(int x, int y, int C, int S) { return (x * S + y * C + 8192) >> 14; }
+
+    // a = 128 h + l, l in [-64, 63]; returns the three digit bytes h, l, h + l.
+    __device__ static __forceinline__ void split(int a, uint32_t& h, uint32_t& l, uint32_t& m) {
+        const int lo = ((a + 64) & 127) - 64;
+        const int hi = (a - lo) >> 7;
+        h = static_cast<uint32_t>(hi) & 0xffu;
+        l = static_cast<uint32_t>(lo) & 0xffu;
+        m = static_cast<uint32_t>(hi + lo) & 0xffu;
+    }
+
+    // Rotate 4 pairs (one uint4 of int16) with 4 (C, S) pairs and split into digits:
+    // 8 bytes per plane returned as two dwords each.
+    __device__ static __forceinline__ void rotate_split8(const uint4& raw, const uint4& cs, uint2& h, uint2& l,
+                                                         uint2& m) {
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint32_t t[4] = {cs.x, cs.y, cs.z, cs.w};
+        uint32_t hb[2] = {0, 0}, lb[2] = {0, 0}, mb[2] = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int x = i16_lo(w[j]), y = i16_hi(w[j]);
+            const int C = i16_lo(t[j]), S = i16_hi(t[j]);
+            const int xr = rot_x(x, y, C, S), yr = rot_y(x, y, C, S);
+            uint32_t a0, a1, a2, b0, b1, b2;
+            split(xr, a0, a1, a2);
+            split(yr, b0, b1, b2);
+            const int sh = 16 * (j & 1);
+            hb[j >> 1] |= (a0 | (b0 << 8)) << sh;
+            lb[j >> 1] |= (a1 | (b1 << 8)) << sh;
+            mb[j >> 1] |= (a2 | (b2 << 8)) << sh;
+        }
+        h = make_uint2(hb[0], hb[1]);
+        l = make_uint2(lb[0], lb[1]);
+        m = make_uint2(mb[0], mb[1]);
+    }
+
+    __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
+        const int lh = (threadIdx.x & 63) >> 5;
+        const bool ok = qi < c.S;
+        const int16_t* src = static_cast<const int16_t*>(a.q) + (ok ? q_index(a, c, qi, D) : 0);
+        const int16_t* tab = a.rope_q14 + static_cast<size_t>(ok ? c.off + qi : 0) * D;
+        q.scale = scale;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const int d0 = 32 * ks + 16 * lh;
+            uint2 h[2], l[2], m[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                uint4 raw = make_uint4(0, 0, 0, 0), cs = raw;
+                if (ok) {
+                    raw = *reinterpret_cast<const uint4*>(src + d0 + 8 * half);
+                    cs = *reinterpret_cast<const uint4*>(tab + d0 + 8 * half);
+                }
+                rotate_split8(raw, cs, h[half], l[half], m[half]);
+            }
+            q.h[ks] = i32x4{(int)h[0].x, (int)h[0].y, (int)h[1].x, (int)h[1].y};
+            q.l[ks] = i32x4{(int)l[0].x, (int)l[0].y, (int)l[1].x, (int)l[1].y};
+            q.m[ks] = i32x4{(int)m[0].x, (int)m[0].y, (int)m[1].x, (int)m[1].y};
+        }
+    }
+
+    __device__ static __forceinline__ void load_k(const RunArgs& a, const Ctx& c, int tile, KRegs& r) {
+        const int16_t* k = static_cast<const int16_t*>(a.k);
+#pragma unroll
+        for (int it = 0; it < D / 32; ++it) {
+            const int idx = threadIdx.x + kThreads * it;
+            const int row = idx / (D / 8), ch = idx % (D / 8);
+            const int key = tile * BN + row;
+            if (key < c.S) {
+                r.raw[it] = *reinterpret_cast<const uint4*>(k + kv_index(a, c, key, D) + 8 * ch);
+                r.cs[it] = *reinterpret_cast<const uint4*>(a.rope_q14 + static_cast<size_t>(c.off + key) * D + 8 * ch);
+            } else {
+                r.raw[it] = make_uint4(0, 0, 0, 0);
+                r.cs[it] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+
+    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
+#pragma unroll
+        for (int it = 0; it < D / 32; ++it) {
+            const int idx = threadIdx.x + kThreads * it;
+            const int row = idx / (D / 8), ch = idx % (D / 8);
+            uint2 h, l, m;
+            rotate_split8(r.raw[it], r.cs[it], h, l, m);
+            char* p = lds + row * kRow + 8 * ch;
+            *reinterpret_cast<uint2*>(p) = h;
+            *reinterpret_cast<uint2*>(p + kPlane) = l;
+            *reinterpret_cast<uint2*>(p + 2 * kPlane) = m;
+        }
+    }
+
+    // Exact int32 scores S^T for key block kb: 2^14 hh + 2^7 (mm - hh - ll) + ll.
+    __device__ static __forceinline__ void qk_i32(const char* lds, int kb, const Q& q, int (&s)[16], int lq,
+                                                  int lh) {
+        const char* row = lds + (32 * kb + lq) * kRow + 16 * lh;
+        i32x16 hh = {}, ll = {}, mm = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const i32x4 ah = *reinterpret_cast<const i32x4*>(row + 32 * ks);
+            const i32x4 al = *reinterpret_cast<const i32x4*>(row + kPlane + 32 * ks);
+            const i32x4 am = *reinterpret_cast<const i32x4*>(row + 2 * kPlane + 32 * ks);
+            hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah, q.h[ks], hh, 0, 0, 0);
+            ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(al, q.l[ks], ll, 0, 0, 0);
+            mm = __builtin_amdgcn_mfma_i32_32x32x32_i8(am, q.m[ks], mm, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const uint32_t h = static_cast<uint32_t>(hh[v]), l = static_cast<uint32_t>(ll[v]);
+            const uint32_t m = static_cast<uint32_t>(mm[v]);
+            s[v] = static_cast<int>((h << 14) + ((m - h - l) << 7) + l);
+        }
+    }
+
+    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float (&s)[16], int lq, int lh) {
+        int si[16];
+        qk_i32(lds, kb, q, si, lq, lh);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = static_cast<float>(si[v]) * q.scale;
+    }
+};
+
+// ------------------------------------------------ fused kernel (f16 P.V)
+
+template <int D, template <int> class QK>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(RunArgs a, float logit_scale) {
+    using P = QK<D>;
+    using V = VStage<D>;
+    constexpr int kStage = P::kBytes + V::kBytes;
+    __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
+
+    Ctx c;
+    if (!make_ctx(a, c)) {
+        zero_rows<D>(a, c);
+        return;
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lq = lane & 31, lh = lane >> 5;
+    const int qw0 = c.q0 + 32 * w;  // this wave's first query row
+    const int n_tiles = (min(c.q0 + BM, c.S) + BN - 1) / BN;
+
+    typename P::KRegs kr;
+    typename V::Regs vr;
+    P::load_k(a, c, 0, kr);
+    V::load(a, c, 0, vr);
+
+    typename P::Q q;
+    P::load_q(a, c, qw0 + lq, logit_scale, q);
+
+    P::commit_k(kr, lds);
+    V::commit(vr, reinterpret_cast<_Float16*>(lds + P::kBytes));
+    __syncthreads();
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    float m_run = kNegInf, l_run = 0.f;
+    const uint32_t ones = pack_h2(1.f, 1.f);
+
+    for (int t = 0; t < n_tiles; ++t) {
+        const bool more = t + 1 < n_tiles;
+        if (more) {
+            P::load_k(a, c, t + 1, kr);
+            V::load(a, c, t + 1, vr);
+        }
+        const char* kbuf = lds + (t & 1) * kStage;
+        const _Float16* vbuf = reinterpret_cast<const _Float16*>(kbuf + P::kBytes);
+
+        const int kt0 = t * BN;
+        int nact = kt0 + 32 <= qw0 + 31 ? 2 : (kt0 <= qw0 + 31 ? 1 : 0);
+        if (qw0 >= c.S) nact = 0;
+        if (nact > 0) {
+            float s[2][16];
+            P::qk(kbuf, 0, q, s[0], lq, lh);
+            if (nact > 1) P::qk(kbuf, 1, q, s[1], lq, lh);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int k0 = kt0 + 32 * kb;
+                if (kb < nact && k0 + 31 > qw0) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (k0 + acc_row(v, lh) > qw0 + lq) s[kb][v] = kNegInf;
+                }
+            }
+            float mx = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb < nact) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+                }
+            mx = halves_max(mx);
+            const float m_new = fmaxf(m_run, mx);
+            if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack)) {
+                const float alpha = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb < nact) {
+                    uint32_t pk[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        pk[j] = pack_h2(fast_exp2(s[kb][2 * j] - m_run), fast_exp2(s[kb][2 * j + 1] - m_run));
+                        l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[j]),
+                                                       __builtin_bit_cast(f16x2, ones), l_run, false);
+                    }
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2) {
+                        const u32x4 b4 = {pk[4 * k2], pk[4 * k2 + 1], pk[4 * k2 + 2], pk[4 * k2 + 3]};
+                        V::pv(vbuf, 2 * kb + k2, __builtin_bit_cast(f16x8, b4), o, lq, lh);
+                    }
+                }
+        }
+        if (more) {
+            char* nbuf = lds + ((t + 1) & 1) * kStage;
+            P::commit_k(kr, nbuf);
+            V::commit(vr, reinterpret_cast<_Float16*>(nbuf + P::kBytes));
+        }
+        __syncthreads();
+    }
+
+    if (qw0 >= c.S) return;
+    const float inv = 1.0f / halves_sum(l_run);
+    const int qi = qw0 + lq;
+    if (qi < c.S) {
+        float* orow = a.out + q_index(a, c, qi, D);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 val = make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                                               o[db][4 * g + 3] * inv);
+                *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * lh) = val;
+            }
+    }
+}
+
+// ------------------------------------------------ fp32 kernel (fp32 matrix cores)
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(RunArgs a, float logit_scale) {
+    constexpr int kStride = D + 4;
+    __shared__ __attribute__((aligned(16))) float ks_[BN * kStride];
+    __shared__ __attribute__((aligned(16))) float vs_[BN * kStride];
+
+    Ctx c;
+    if (!make_ctx(a, c)) {
+        zero_rows<D>(a, c);
+        return;
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lq = lane & 31, lh = lane >> 5;
+    const int qw0 = c.q0 + 32 * w;
+    const int n_tiles = (min(c.q0 + BM, c.S) + BN - 1) / BN;
+    const float* qg = static_cast<const float*>(a.q);
+    const float* kg = static_cast<const float*>(a.k);
+    const float* vg = static_cast<const float*>(a.v);
+
+    // Q' of query qw0+lq: lane half lh keeps component lh of every pair (d = 2ks + lh).
+    float qv[D / 2];
+    {
+        const int qi = qw0 + lq;
+        const bool ok = qi < c.S;
+#pragma unroll
+        for (int k = 0; k < D / 2; ++k) {
+            float x = 0.f, y = 0.f, cs = 0.f, sn = 0.f;
+            if (ok) {
+                const float2 xy = *reinterpret_cast<const float2*>(qg + q_index(a, c, qi, D) + 2 * k);
+                const float2 t = *reinterpret_cast<const float2*>(a.rope_f32 + static_cast<size_t>(c.off + qi) * D + 2 * k);
+                x = xy.x, y = xy.y, cs = t.x, sn = t.y;
+            }
+            qv[k] = (lh ? fmaf(x, sn, y * cs) : fmaf(x, cs, -y * sn)) * logit_scale;
+        }
+    }
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    float m_run = kNegInf, l_run = 0.f;
+
+    for (int t = 0; t < n_tiles; ++t) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < BN * (D / 4); idx += kThreads) {
+            const int row = idx / (D / 4), ch = idx % (D / 4);
+            const int key = t * BN + row;
+            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx, tc = kx;
+            if (key < c.S) {
+                kx = *reinterpret_cast<const float4*>(kg + kv_index(a, c, key, D) + 4 * ch);
+                vx = *reinterpret_cast<const float4*>(vg + kv_index(a, c, key, D) + 4 * ch);
+                tc = *reinterpret_cast<const float4*>(a.rope_f32 + static_cast<size_t>(c.off + key) * D + 4 * ch);
+            }
+            const float4 kr = make_float4(fmaf(kx.x, tc.x, -kx.y * tc.y), fmaf(kx.x, tc.y, kx.y * tc.x),
+                                          fmaf(kx.z, tc.z, -kx.w * tc.w), fmaf(kx.z, tc.w, kx.w * tc.z));
+            *reinterpret_cast<float4*>(ks_ + row * kStride + 4 * ch) = kr;
+            *reinterpret_cast<float4*>(vs_ + row * kStride + 4 * ch) = vx;
+        }
+        __syncthreads();
+        const int kt0 = t * BN;
+        int nact = kt0 + 32 <= qw0 + 31 ? 2 : (kt0 <= qw0 + 31 ? 1 : 0);
+        if (qw0 >= c.S) nact = 0;
+        if (nact == 0) continue;
+        float s[2][16];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (kb >= nact) break;
+            f32x16 acc = {};
+            const float* row = ks_ + (32 * kb + lq) * kStride + lh;
+#pragma unroll
+            for (int k = 0; k < D / 2; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(row[2 * k], qv[k], acc, 0, 0, 0);
+            const int k0 = kt0 + 32 * kb;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[kb][v] = (k0 + acc_row(v, lh) > qw0 + lq) ? kNegInf : acc[v];
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb < nact) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+            }
+        mx = halves_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack)) {
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (kb >= nact) break;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = fast_exp2(s[kb][v] - m_run);
+                l_run += p;
+                const float* vrow = vs_ + (32 * kb + acc_row(v, lh)) * kStride + lq;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * db], p, o[db], 0, 0, 0);
+            }
+        }
+    }
+
+    if (qw0 >= c.S) return;
+    const float inv = 1.0f / halves_sum(l_run);
+    const int qi = qw0 + lq;
+    if (qi < c.S) {
+        float* orow = a.out + q_index(a, c, qi, D);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 val = make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                                               o[db][4 * g + 3] * inv);
+                *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * lh) = val;
+            }
+    }
+}
+
+// ------------------------------------------------ int16 test kernels
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void debug_rope_i16_kernel(RunArgs a, int n_heads_x, int16_t* dst) {
+    const size_t pair = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const size_t total = static_cast<size_t>(a.batch) * a.seq_len * n_heads_x * (D / 2);
+    if (pair >= total) return;
+    const int k = static_cast<int>(pair % (D / 2));
+    size_t rest = pair / (D / 2);
+    rest /= n_heads_x;
+    const int i = static_cast<int>(rest % a.seq_len);
+    const int b = static_cast<int>(rest / a.seq_len);
+    const int off = a.pos_offsets ? a.pos_offsets[b] : 0;
+    const int16_t* src = static_cast<const int16_t*>(a.q);
+    if (off < 0 || static_cast<long long>(off) + a.seq_len > a.max_seq) {
+        dst[2 * pair] = 0;
+        dst[2 * pair + 1] = 0;
+        atomicOr(a.status, 1);
+        return;
+    }
+    const int x = src[2 * pair], y = src[2 * pair + 1];
+    const int16_t* t = a.rope_q14 + static_cast<size_t>(off + i) * D + 2 * k;
+    dst[2 * pair] = static_cast<int16_t>(I16QK<D>::rot_x(x, y, t[0], t[1]));
+    dst[2 * pair + 1] = static_cast<int16_t>(I16QK<D>::rot_y(x, y, t[0], t[1]));
+}
+
+// Full (unmasked) int32 score matrix through the same staging and MFMA code.
+template <int D>
+__global__ __launch_bounds__(kThreads) void debug_scores_i32_kernel(RunArgs a, int32_t* dst) {
+    using P = I16QK<D>;
+    __shared__ __attribute__((aligned(16))) char lds[P::kBytes];
+    Ctx c;
+    if (!make_ctx(a, c)) {
+        if (threadIdx.x == 0) atomicOr(a.status, 1);
+        return;
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lq = lane & 31, lh = lane >> 5;
+    const int qw0 = c.q0 + 32 * w;
+    typename P::Q q;
+    P::load_q(a, c, qw0 + lq, 1.0f, q);
+    const int n_tiles = (c.S + BN - 1) / BN;
+    for (int t = 0; t < n_tiles; ++t) {
+        typename P::KRegs kr;
+        P::load_k(a, c, t, kr);
+        __syncthreads();
+        P::commit_k(kr, lds);
+        __syncthreads();
+        const int qi = qw0 + lq;
+        if (qi >= c.S) continue;
+        int32_t* row = dst + ((static_cast<size_t>(c.b) * a.n_heads + c.hq) * c.S + qi) * c.S;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            int s[16];
+            P::qk_i32(lds, kb, q, s, lq, lh);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = t * BN + 32 * kb + acc_row(v, lh);
+                if (key < c.S) row[key] = s[v];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------ launch helpers
+
+dim3 grid_for(const RunArgs& a) {
+    const int n_qblocks = (a.seq_len + BM - 1) / BM;
+    return dim3(static_cast<unsigned>(n_qblocks) * a.batch * a.n_heads);
+}
+
+template <int D>
+hipError_t launch_bf16_d(const RunArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16QK>), grid_for(a), dim3(kThreads), 0, s, a, a.score_scale * kLog2e);
+    return hipGetLastError();
+}
+template <int D>
+hipError_t launch_i16_d(const RunArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, I16QK>), grid_for(a), dim3(kThreads), 0, s, a, a.score_scale * kLog2e);
+    return hipGetLastError();
+}
+template <int D>
+hipError_t launch_f32_d(const RunArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), grid_for(a), dim3(kThreads), 0, s, a, a.score_scale * kLog2e);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#define PA_DISPATCH_D(fn, d, ...)                       \
+    switch (d) {                                        \
+        case 64: return fn<64>(__VA_ARGS__);            \
+        case 96: return fn<96>(__VA_ARGS__);            \
+        case 128: return fn<128>(__VA_ARGS__);          \
+        default: return hipErrorInvalidValue;           \
+    }
+
+hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_bf16_d, head_dim, a, s) }
+hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_i16_d, head_dim, a, s) }
+hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_f32_d, head_dim, a, s) }
+
+namespace {
+template <int D>
+hipError_t launch_rope_d(const RunArgs& a, int n_heads_x, int16_t* dst, hipStream_t s) {
+    const size_t pairs = static_cast<size_t>(a.batch) * a.seq_len * n_heads_x * (D / 2);
+    const size_t blocks = (pairs + kThreads - 1) / kThreads;
+    if (blocks > 0x7fffffffu) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((debug_rope_i16_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a,
+                       n_heads_x, dst);
+    return hipGetLastError();
+}
+template <int D>
+hipError_t launch_scores_d(const RunArgs& a, int32_t* dst, hipStream_t s) {
+    hipLaunchKernelGGL((debug_scores_i32_kernel<D>), grid_for(a), dim3(kThreads), 0, s, a, dst);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_debug_rope_i16(int head_dim, const RunArgs& a, int n_heads_x, int16_t* dst, hipStream_t s) {
+    PA_DISPATCH_D(launch_rope_d, head_dim, a, n_heads_x, dst, s)
+}
+hipError_t launch_debug_scores_i32(int head_dim, const RunArgs& a, int32_t* dst, hipStream_t s) {
+    PA_DISPATCH_D(launch_scores_d, head_dim, a, dst, s)
+}
+
+}  // namespace pa

@@ -1,0 +1,37 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything one fused attention launch needs.  Pointers are device pointers.
+struct RunArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* pos_offsets;  // may be null: all offsets 0
+    float* out;
+    const float* rope_f32;       // [max_seq][head_dim/2] (cos, sin) fp32 pairs
+    const int16_t* rope_q14;     // [max_seq][head_dim/2] (C, S) Q1.14 pairs
+    int* status;                 // set non-zero when a position leaves the table
+    int batch;
+    int seq_len;
+    int n_heads;
+    int n_kv_heads;
+    int max_seq;
+    float score_scale;           // resolved (never 0 here)
+};
+
+hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t stream);
+hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t stream);
+hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t stream);
+
+// Int16 test exports; RunArgs.q is the tensor to rotate (x) for the rope one,
+// q/k for the scores one; `dst` receives int16 x_rot or int32 scores.
+hipError_t launch_debug_rope_i16(int head_dim, const RunArgs& a, int n_heads_x, int16_t* dst,
+                                 hipStream_t stream);
+hipError_t launch_debug_scores_i32(int head_dim, const RunArgs& a, int32_t* dst, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 CPU oracle.
+
+Small cases compare every element; full-size workloads compare sampled output
+rows (each computed by the oracle one at a time) plus whole heads.  Floating
+tolerances: fp32 inputs max-abs 1e-5; bf16 inputs and the int16 variant's
+output max-abs 1e-2 and mean-abs 1e-3.  The int16 rotation and int32 scores are
+compared bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rope_causal_attention_amd as pa
+import synth
+from gpu_common import (announce, assert_close, errors, need_gpu, oracle_full, oracle_rows, run_gpu, sample_rows,
+                        to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+# ------------------------------------------------------------ float, whole O
+
+SMALL_CASES = [
+    # name, batch, Hq, Hkv, S, D, dtype, theta, offsets
+    ("tiny_f32", 1, 1, 1, 32, 64, "f32", 1e4, None),
+    ("f32_ragged_d96_gqa", 2, 4, 2, 77, 96, "f32", 1e4, [0, 5]),
+    ("f32_d128_2blocks", 1, 2, 1, 200, 128, "f32", 1e6, None),
+    ("bf16_d64_ragged", 2, 3, 3, 301, 64, "bf16", 1e4, [0, 17]),
+    ("bf16_d96_ragged", 1, 4, 2, 333, 96, "bf16", 1e4, None),
+    ("bf16_d128_ragged", 1, 2, 2, 390, 128, "bf16", 1e6, [100]),
+    ("bf16_d128_s1", 3, 2, 1, 1, 128, "bf16", 1e4, None),
+    ("bf16_d96_s33", 1, 2, 2, 33, 96, "bf16", 1e4, None),
+    ("bf16_d64_s129", 1, 8, 8, 129, 64, "bf16", 1e4, None),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_float_small_full_compare(case):
+    name, B, Hq, Hkv, S, D, dt, theta, offs = case
+    announce(name)
+    max_seq = S + (max(offs) if offs else 0)
+    w = synth.Workload(name, B, Hq, Hkv, S, D, dt, theta, seed=hash(name) % 10000, max_seq=max_seq)
+    q, k, v = synth.make_inputs(w)
+    got = run_gpu(w, q, k, v, pos_offsets=offs)
+    want = oracle_full(w, q, k, v, pos_offsets=offs)
+    mx, mean = assert_close(got.numpy(), want, dt)
+    announce(name, f"max {mx:.2e} mean {mean:.2e}")
+
+
+def test_tiny_workload_exact_config():
+    w = synth.WORKLOADS["tiny_f32_s32_d64"]
+    announce(w.name)
+    q, k, v = synth.make_inputs(w)
+    got = run_gpu(w, q, k, v)
+    want = oracle_full(w, q, k, v)
+    assert_close(got.numpy(), want, "f32")
+
+
+@pytest.mark.parametrize("name", ["mha_bf16_h32_s512_d128", "gqa_bf16_b16_h16kv8_s512_d128"])
+def test_full_workload_whole_output(name):
+    w = synth.WORKLOADS[name]
+    announce(name)
+    q, k, v = synth.make_inputs(w)
+    got = run_gpu(w, q, k, v)
+    want = oracle_full(w, q, k, v)
+    mx, mean = assert_close(got.numpy(), want, w.dtype)
+    announce(name, f"max {mx:.2e} mean {mean:.2e}")
+
+
+@pytest.mark.parametrize("reading", ["independent", "shared"])
+def test_long_prompt_workload(reading):
+    """seq 4096, D 96, per-head scales: 3 whole heads plus rows sampled over all heads."""
+    w = synth.workload("mha_bf16_h32_s4096_d96", head_scale=reading)
+    announce(w.name, reading)
+    q, k, v = synth.make_inputs(w)
+    got = run_gpu(w, q, k, v).numpy()
+    worst = []
+    for h in (0, 17, 31):
+        one = synth.workload("mha_bf16_h32_s4096_d96", n_heads=1, n_kv_heads=1)
+        want = oracle_full(one, q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1])
+        worst.append(assert_close(got[:, :, h:h + 1], want, "bf16"))
+    rows = sample_rows(w, 96, seed=7)
+    want = oracle_rows(w, q, k, v, rows)
+    sel = np.stack([got[b, i, h] for b, h, i in rows])
+    mx, _ = errors(sel, want)
+    assert mx <= 1e-2, f"sampled rows max-abs {mx:.3e}"
+    announce(w.name, reading, "heads", [f"{a:.2e}/{b:.2e}" for a, b in worst], f"rows max {mx:.2e}")
+
+
+# ------------------------------------------------------------ int16 variant
+
+def _i16_handle(w, max_seq=None):
+    return pa.PrefillAttention(w.n_heads, w.n_kv_heads, w.head_dim, max_seq or w.seq_len, w.rope_theta)
+
+
+@pytest.mark.parametrize("offs", [None, [3]])
+def test_int16_rotation_bit_exact_all_heads(offs):
+    w = synth.WORKLOADS["i16_h32_s2048_d128"]
+    announce("i16 rope", offs)
+    q, k, v = synth.make_inputs(w)
+    max_seq = w.seq_len + (offs[0] if offs else 0)
+    attn = _i16_handle(w, max_seq)
+    try:
+        off_d = None if offs is None else torch.tensor(offs, dtype=torch.int32, device="cuda")
+        for name, x in (("q", q), ("k", k)):
+            xd = x.cuda()
+            xr = torch.empty_like(xd)
+            pa.prefill_attn_debug_rope_i16(attn.handle, w.batch, w.seq_len, xd, x.shape[2], off_d, xr)
+            torch.cuda.synchronize()
+            pos = np.arange(w.seq_len) + (offs[0] if offs else 0)
+            want = oracle.rope_rotate_i16(x[0].numpy(), pos, w.rope_theta)
+            assert np.array_equal(xr.cpu()[0].numpy().astype(np.int64), want), name
+    finally:
+        attn.close()
+
+
+def test_int16_scores_bit_exact():
+    w = synth.WORKLOADS["i16_h32_s2048_d128"]
+    announce("i16 scores")
+    q, k, v = synth.make_inputs(w)
+    attn = _i16_handle(w)
+    try:
+        qd, kd = to_dev(q, k)
+        sc = torch.empty((w.batch, w.n_heads, w.seq_len, w.seq_len), dtype=torch.int32, device="cuda")
+        pa.prefill_attn_debug_scores_i32(attn.handle, w.batch, w.seq_len, qd, kd, None, sc)
+        torch.cuda.synchronize()
+        pos = np.arange(w.seq_len)
+        qr = oracle.rope_rotate_i16(q[0].numpy(), pos, w.rope_theta)
+        kr = oracle.rope_rotate_i16(k[0].numpy(), pos, w.rope_theta)
+        for h in range(w.n_heads):
+            want = oracle.scores_i32(qr[:, h], kr[:, h])
+            got = sc[0, h].cpu().numpy().astype(np.int64)
+            assert np.array_equal(got, want), f"head {h}: {np.count_nonzero(got != want)} mismatches"
+    finally:
+        attn.close()
+
+
+def test_int16_scores_ragged_gqa_offsets():
+    w = synth.Workload("i16_small", 2, 4, 2, 150, 64, "i16", 1e4, 77, score_scale=2.0 ** -22 / 8)
+    announce(w.name)
+    q, k, v = synth.make_inputs(w)
+    offs = [0, 40]
+    attn = pa.PrefillAttention(4, 2, 64, 190, 1e4)
+    try:
+        qd, kd = to_dev(q, k)
+        od = torch.tensor(offs, dtype=torch.int32, device="cuda")
+        sc = torch.empty((2, 4, 150, 150), dtype=torch.int32, device="cuda")
+        pa.prefill_attn_debug_scores_i32(attn.handle, 2, 150, qd, kd, od, sc)
+        torch.cuda.synchronize()
+        for b in range(2):
+            pos = np.arange(150) + offs[b]
+            qr = oracle.rope_rotate_i16(q[b].numpy(), pos, 1e4)
+            kr = oracle.rope_rotate_i16(k[b].numpy(), pos, 1e4)
+            for h in range(4):
+                assert np.array_equal(sc[b, h].cpu().numpy().astype(np.int64), oracle.scores_i32(qr[:, h], kr[:, h // 2]))
+    finally:
+        attn.close()
+
+
+def test_int16_attention_output():
+    w = synth.WORKLOADS["i16_h32_s2048_d128"]
+    announce(w.name)
+    q, k, v = synth.make_inputs(w)
+    got = run_gpu(w, q, k, v).numpy()
+    for h in (0, 31):
+        one = synth.workload(w.name, n_heads=1, n_kv_heads=1)
+        want = oracle_full(one, q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1])
+        assert_close(got[:, :, h:h + 1], want, "bf16")
+    rows = sample_rows(w, 64, seed=9)
+    want = oracle_rows(w, q, k, v, rows)
+    sel = np.stack([got[b, i, h] for b, h, i in rows])
+    mx, _ = errors(sel, want)
+    assert mx <= 1e-2
+
+
+def test_int16_degenerate_scale_small():
+    """A large score scale makes the softmax nearly one-hot: exercises ties and argmax."""
+    w = synth.Workload("i16_sharp", 1, 2, 2, 130, 128, "i16", 1e4, 88, score_scale=2.0 ** -8 / 11.3137085)
+    announce(w.name)
+    q, k, v = synth.make_inputs(w)
+    got = run_gpu(w, q, k, v)
+    want = oracle_full(w, q, k, v)
+    assert_close(got.numpy(), want, "bf16")
