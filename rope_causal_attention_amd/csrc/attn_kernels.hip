@@ -93,6 +93,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // half lh: rows come in groups of 4, interleaved between the two halves.
 __device__ __forceinline__ int acc_row(int v, int lh) { return 8 * (v >> 2) + 4 * lh + (v & 3); }
 
+// 16-byte load at a byte offset from a workgroup-uniform base (32-bit offset).
+__device__ __forceinline__ uint4 ld16(const char* base, uint32_t off) {
+    return *reinterpret_cast<const uint4*>(base + off);
+}
+__device__ __forceinline__ float4 ld16f(const char* base, uint32_t off) {
+    return *reinterpret_cast<const float4*>(base + off);
+}
+
 // Work order: longest query blocks first; when the (batch, head) count is a
 // multiple of 8, consecutive workgroup ids (dealt round-robin to the 8 XCDs)
 // are mapped so that each XCD owns a contiguous range of (batch, head).
@@ -118,6 +126,7 @@ struct Ctx {
     int b, hq, hkv, off, S, q0;
 };
 
+template <int BM>
 __device__ __forceinline__ bool make_ctx(const RunArgs& a, Ctx& c) {
     const int n_qblocks = (a.seq_len + BM - 1) / BM;
     const BlockPos bp = map_block(n_qblocks, a.batch, a.n_heads);
@@ -137,11 +146,23 @@ __device__ __forceinline__ size_t kv_index(const RunArgs& a, const Ctx& c, int j
     return ((static_cast<size_t>(c.b) * c.S + j) * a.n_kv_heads + c.hkv) * D;
 }
 
+// Rows of one (batch, head) of a [B][S][H][D] tensor: uniform base + 32-bit byte offsets.
+struct Rows {
+    const char* base;
+    uint32_t stride;  // bytes between consecutive tokens
+};
+__device__ __forceinline__ Rows kv_rows(const RunArgs& a, const Ctx& c, const void* t, int D, int el) {
+    return {static_cast<const char*>(t) + kv_index(a, c, 0, D) * el, static_cast<uint32_t>(a.n_kv_heads * D * el)};
+}
+__device__ __forceinline__ Rows q_rows(const RunArgs& a, const Ctx& c, const void* t, int D, int el) {
+    return {static_cast<const char*>(t) + q_index(a, c, 0, D) * el, static_cast<uint32_t>(a.n_heads * D * el)};
+}
+
 // A batch element whose positions leave the tables: O = 0 and the status word is set.
-template <int D>
+template <int D, int BM, int NT>
 __device__ void zero_rows(const RunArgs& a, const Ctx& c) {
     const int rows = min(BM, c.S - c.q0);
-    for (int idx = threadIdx.x; idx < rows * (D / 4); idx += kThreads) {
+    for (int idx = threadIdx.x; idx < rows * (D / 4); idx += NT) {
         const int r = idx / (D / 4), col = idx % (D / 4);
         float4* dst = reinterpret_cast<float4*>(a.out + q_index(a, c, c.q0 + r, D)) + col;
         *dst = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -151,48 +172,61 @@ __device__ void zero_rows(const RunArgs& a, const Ctx& c) {
 
 // ------------------------------------------------ V tile: bf16 -> f16, transposed
 
-// LDS holds V^T [D][BN + 8] f16.  Thread (kq, dc) reads keys 4kq..4kq+3 at
+// LDS holds V^T [D][BN + 8] f16.  Work item (kq, dc) reads keys 4kq..4kq+3 at
 // dims 8dc..8dc+7; converting two keys at a time yields (key, key+1) pairs of
 // one dim, i.e. the transpose for free.  Key quads are stored in the order
 // 0,2,1,3 within each 16-key group so that the 8 keys one lane half feeds to
-// a 16-deep MFMA step are contiguous (16-byte LDS reads).
-template <int D>
+// a 16-deep MFMA step are contiguous (16-byte LDS reads).  Keys past the end
+// of the sequence are clamped to the last row: they only ever meet masked
+// (zero) probabilities, and a real row keeps every value finite.
+template <int D, int NT>
 struct VStage {
     static constexpr int kStride = BN + 8;  // f16 per V^T row
     static constexpr int kBytes = D * kStride * 2;
+    static constexpr int kItems = 2 * D;    // 16 key quads x D/8 dim chunks
+    static constexpr int kPer = (kItems + NT - 1) / NT;
     struct Regs {
-        uint4 raw[4];
+        uint4 raw[kPer][4];
     };
-    __device__ static __forceinline__ void load(const RunArgs& a, const Ctx& c, int tile, Regs& r) {
-        const int tid = threadIdx.x;
-        if (tid >= 2 * D) return;
-        const int kq = tid & 15, dc = tid >> 4;
-        const uint16_t* v = static_cast<const uint16_t*>(a.v);
+    __device__ static __forceinline__ bool has(int i) { return kItems % NT == 0 || static_cast<int>(threadIdx.x % NT) + NT * i < kItems; }
+    // Loads are unconditional (surplus threads re-read the last item) so that no
+    // branch separates a load from its use; only the commit is guarded.
+    template <bool CLAMP>
+    __device__ static __forceinline__ void load(const Rows& p, int S, int tile, Regs& r) {
+        const char* vb = p.base + static_cast<size_t>(tile * BN) * p.stride;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int key = tile * BN + 4 * kq + rr;
-            r.raw[rr] = key < c.S ? *reinterpret_cast<const uint4*>(v + kv_index(a, c, key, D) + 8 * dc)
-                                  : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < kPer; ++i) {
+            const int idx = min(static_cast<int>(threadIdx.x % NT) + NT * i, kItems - 1);
+            const int kq = idx & 15, dc = idx >> 4;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                int row = 4 * kq + rr;
+                if (CLAMP) row = min(row, S - 1 - tile * BN);
+                r.raw[i][rr] = ld16(vb, row * p.stride + 16 * dc);
+            }
         }
     }
     __device__ static __forceinline__ uint32_t word(const uint4& u, int i) {
         return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
     }
     __device__ static __forceinline__ void commit(const Regs& r, _Float16* lds) {
-        const int tid = threadIdx.x;
-        if (tid >= 2 * D) return;
-        const int kq = tid & 15, dc = tid >> 4;
-        const int pos = (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x[4];
+        for (int i = 0; i < kPer; ++i) {
+            if (!has(i)) continue;
+            const int idx = static_cast<int>(threadIdx.x % NT) + NT * i;
+            const int kq = idx & 15, dc = idx >> 4;
+            const int pos = (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const uint32_t w = word(r.raw[rr], e >> 1);
-                x[rr] = (e & 1) ? bf_hi(w) : bf_lo(w);
+            for (int e = 0; e < 8; ++e) {
+                float x[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const uint32_t w = word(r.raw[i][rr], e >> 1);
+                    x[rr] = (e & 1) ? bf_hi(w) : bf_lo(w);
+                }
+                uint2 pk = make_uint2(pack_h2(x[0], x[1]), pack_h2(x[2], x[3]));
+                *reinterpret_cast<uint2*>(lds + (8 * dc + e) * kStride + 4 * pos) = pk;
             }
-            uint2 pk = make_uint2(pack_h2(x[0], x[1]), pack_h2(x[2], x[3]));
-            *reinterpret_cast<uint2*>(lds + (8 * dc + e) * kStride + 4 * pos) = pk;
         }
     }
     // O^T[db] += V^T[32db.., 16kk..] . P^T for the 16-key step kk (0..3) of the tile.
@@ -208,16 +242,23 @@ struct VStage {
 
 // ------------------------------------------------ Q.K^T policy: bf16 inputs
 
-template <int D>
+template <int D, int NT>
 struct Bf16QK {
     static constexpr int kStride = D + 8;  // f16 per K' row (16-byte pad against bank conflicts)
     static constexpr int kBytes = BN * kStride * 2;
+    static constexpr int kChunks = BN * D / 8;  // 16-byte chunks per K tile
+    static constexpr int kPer = (kChunks + NT - 1) / NT;
     struct Q {
         f16x8 f[D / 16];
     };
     struct KRegs {
-        uint4 raw[D / 32];
-        float4 cs[D / 32][2];
+        uint4 raw[kPer];
+        float4 c0[kPer], c1[kPer];
+    };
+    struct KPtr {
+        Rows k;
+        const char* tab;  // table row of position off[b]
+        int S;
     };
 
     // Rotate 4 adjacent pairs: x' = x c - y s, y' = x s + y c; times `scale`.
@@ -236,63 +277,71 @@ struct Bf16QK {
         return make_uint4(o[0], o[1], o[2], o[3]);
     }
 
+    __device__ static __forceinline__ KPtr kptr(const RunArgs& a, const Ctx& c) {
+        return {kv_rows(a, c, a.k, D, 2), reinterpret_cast<const char*>(a.rope_f32 + static_cast<size_t>(c.off) * D),
+                c.S};
+    }
+
     __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
         const int lh = (threadIdx.x & 63) >> 5;
         const bool ok = qi < c.S;
-        const uint16_t* src = static_cast<const uint16_t*>(a.q) + (ok ? q_index(a, c, qi, D) : 0);
-        const float* tab = a.rope_f32 + static_cast<size_t>(ok ? c.off + qi : 0) * D;
+        const Rows rq = q_rows(a, c, a.q, D, 2);
+        const char* tab = reinterpret_cast<const char*>(a.rope_f32 + static_cast<size_t>(c.off) * D);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             const int d0 = 16 * ks + 8 * lh;
             uint4 raw = make_uint4(0, 0, 0, 0);
             float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0;
             if (ok) {
-                raw = *reinterpret_cast<const uint4*>(src + d0);
-                c0 = *reinterpret_cast<const float4*>(tab + d0);
-                c1 = *reinterpret_cast<const float4*>(tab + d0 + 4);
+                raw = ld16(rq.base, qi * rq.stride + 2 * d0);
+                c0 = ld16f(tab, (qi * D + d0) * 4);
+                c1 = ld16f(tab, (qi * D + d0 + 4) * 4);
             }
             q.f[ks] = __builtin_bit_cast(f16x8, rotate8(raw, c0, c1, scale));
         }
     }
 
-    __device__ static __forceinline__ void load_k(const RunArgs& a, const Ctx& c, int tile, KRegs& r) {
-        const uint16_t* k = static_cast<const uint16_t*>(a.k);
+    __device__ static __forceinline__ bool has(int i) { return kChunks % NT == 0 || static_cast<int>(threadIdx.x % NT) + NT * i < kChunks; }
+
+    // CLAMP: the tile may reach past the last key (rows are clamped to it).
+    template <bool CLAMP>
+    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
+        const char* kb = p.k.base + static_cast<size_t>(tile * BN) * p.k.stride;
+        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
 #pragma unroll
-        for (int it = 0; it < D / 32; ++it) {
-            const int idx = threadIdx.x + kThreads * it;
-            const int row = idx / (D / 8), ch = idx % (D / 8);
-            const int key = tile * BN + row;
-            if (key < c.S) {
-                r.raw[it] = *reinterpret_cast<const uint4*>(k + kv_index(a, c, key, D) + 8 * ch);
-                const float* tab = a.rope_f32 + static_cast<size_t>(c.off + key) * D + 8 * ch;
-                r.cs[it][0] = *reinterpret_cast<const float4*>(tab);
-                r.cs[it][1] = *reinterpret_cast<const float4*>(tab + 4);
-            } else {
-                r.raw[it] = make_uint4(0, 0, 0, 0);
-                r.cs[it][0] = r.cs[it][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+        for (int i = 0; i < kPer; ++i) {
+            const int idx = min(static_cast<int>(threadIdx.x % NT) + NT * i, kChunks - 1);
+            int row = idx / (D / 8);
+            const int ch = idx % (D / 8);
+            if (CLAMP) row = min(row, p.S - 1 - tile * BN);
+            r.raw[i] = ld16(kb, row * p.k.stride + 16 * ch);
+            r.c0[i] = ld16f(tb, (row * D + 8 * ch) * 4);
+            r.c1[i] = ld16f(tb, (row * D + 8 * ch + 4) * 4);
         }
     }
 
     __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
         _Float16* kl = reinterpret_cast<_Float16*>(lds);
 #pragma unroll
-        for (int it = 0; it < D / 32; ++it) {
-            const int idx = threadIdx.x + kThreads * it;
+        for (int i = 0; i < kPer; ++i) {
+            if (!has(i)) continue;
+            const int idx = static_cast<int>(threadIdx.x % NT) + NT * i;
             const int row = idx / (D / 8), ch = idx % (D / 8);
-            *reinterpret_cast<uint4*>(kl + row * kStride + 8 * ch) = rotate8(r.raw[it], r.cs[it][0], r.cs[it][1], 1.0f);
+            *reinterpret_cast<uint4*>(kl + row * kStride + 8 * ch) = rotate8(r.raw[i], r.c0[i], r.c1[i], 1.0f);
         }
     }
 
-    // Logits (log2 units) S^T for key block kb (32 keys) of the tile x this wave's 32 queries.
-    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float (&s)[16], int lq, int lh) {
+    // Logits (log2 units) S^T for key block kb (32 keys) of the tile x this
+    // wave's 32 queries.  All K' fragments of the block are read from LDS
+    // before the MFMA chain is issued.
+    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh) {
         const _Float16* row = reinterpret_cast<const _Float16*>(lds) + (32 * kb + lq) * kStride + 8 * lh;
+        f16x8 a[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) a[ks] = *reinterpret_cast<const f16x8*>(row + 16 * ks);
         f32x16 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const f16x8 a = *reinterpret_cast<const f16x8*>(row + 16 * ks);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, q.f[ks], acc, 0, 0, 0);
-        }
+        for (int ks = 0; ks < D / 16; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], q.f[ks], acc, 0, 0, 0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[v] = acc[v];
     }
@@ -300,18 +349,25 @@ struct Bf16QK {
 
 // ------------------------------------------------ Q.K^T policy: int16 inputs
 
-template <int D>
+template <int D, int NT>
 struct I16QK {
     static constexpr int kRow = D + 16;  // bytes per 8-bit digit row
     static constexpr int kPlane = BN * kRow;
     static constexpr int kBytes = 3 * kPlane;  // planes: high digit, low digit, high + low
+    static constexpr int kChunks = BN * D / 8;
+    static constexpr int kPer = (kChunks + NT - 1) / NT;
     struct Q {
         i32x4 h[D / 32], l[D / 32], m[D / 32];
         float scale;
     };
     struct KRegs {
-        uint4 raw[D / 32];
-        uint4 cs[D / 32];
+        uint4 raw[kPer];
+        uint4 cs[kPer];
+    };
+    struct KPtr {
+        Rows k;
+        const char* tab;
+        int S;
     };
 
     // Fixed-point rotation with round-half-up: (x C - y S + 2^13) >> 14, (x S + y C + 2^13) >> 14.
@@ -352,11 +408,16 @@ struct I16QK {
         m = make_uint2(mb[0], mb[1]);
     }
 
+    __device__ static __forceinline__ KPtr kptr(const RunArgs& a, const Ctx& c) {
+        return {kv_rows(a, c, a.k, D, 2), reinterpret_cast<const char*>(a.rope_q14 + static_cast<size_t>(c.off) * D),
+                c.S};
+    }
+
     __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
         const int lh = (threadIdx.x & 63) >> 5;
         const bool ok = qi < c.S;
-        const int16_t* src = static_cast<const int16_t*>(a.q) + (ok ? q_index(a, c, qi, D) : 0);
-        const int16_t* tab = a.rope_q14 + static_cast<size_t>(ok ? c.off + qi : 0) * D;
+        const Rows rq = q_rows(a, c, a.q, D, 2);
+        const char* tab = reinterpret_cast<const char*>(a.rope_q14 + static_cast<size_t>(c.off) * D);
         q.scale = scale;
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
@@ -366,8 +427,8 @@ struct I16QK {
             for (int half = 0; half < 2; ++half) {
                 uint4 raw = make_uint4(0, 0, 0, 0), cs = raw;
                 if (ok) {
-                    raw = *reinterpret_cast<const uint4*>(src + d0 + 8 * half);
-                    cs = *reinterpret_cast<const uint4*>(tab + d0 + 8 * half);
+                    raw = ld16(rq.base, qi * rq.stride + 2 * (d0 + 8 * half));
+                    cs = ld16(tab, (qi * D + d0 + 8 * half) * 2);
                 }
                 rotate_split8(raw, cs, h[half], l[half], m[half]);
             }
@@ -377,30 +438,31 @@ struct I16QK {
         }
     }
 
-    __device__ static __forceinline__ void load_k(const RunArgs& a, const Ctx& c, int tile, KRegs& r) {
-        const int16_t* k = static_cast<const int16_t*>(a.k);
+    __device__ static __forceinline__ bool has(int i) { return kChunks % NT == 0 || static_cast<int>(threadIdx.x % NT) + NT * i < kChunks; }
+
+    template <bool CLAMP>
+    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
+        const char* kb = p.k.base + static_cast<size_t>(tile * BN) * p.k.stride;
+        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
 #pragma unroll
-        for (int it = 0; it < D / 32; ++it) {
-            const int idx = threadIdx.x + kThreads * it;
-            const int row = idx / (D / 8), ch = idx % (D / 8);
-            const int key = tile * BN + row;
-            if (key < c.S) {
-                r.raw[it] = *reinterpret_cast<const uint4*>(k + kv_index(a, c, key, D) + 8 * ch);
-                r.cs[it] = *reinterpret_cast<const uint4*>(a.rope_q14 + static_cast<size_t>(c.off + key) * D + 8 * ch);
-            } else {
-                r.raw[it] = make_uint4(0, 0, 0, 0);
-                r.cs[it] = make_uint4(0, 0, 0, 0);
-            }
+        for (int i = 0; i < kPer; ++i) {
+            const int idx = min(static_cast<int>(threadIdx.x % NT) + NT * i, kChunks - 1);
+            int row = idx / (D / 8);
+            const int ch = idx % (D / 8);
+            if (CLAMP) row = min(row, p.S - 1 - tile * BN);
+            r.raw[i] = ld16(kb, row * p.k.stride + 16 * ch);
+            r.cs[i] = ld16(tb, (row * D + 8 * ch) * 2);
         }
     }
 
     __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
 #pragma unroll
-        for (int it = 0; it < D / 32; ++it) {
-            const int idx = threadIdx.x + kThreads * it;
+        for (int i = 0; i < kPer; ++i) {
+            if (!has(i)) continue;
+            const int idx = static_cast<int>(threadIdx.x % NT) + NT * i;
             const int row = idx / (D / 8), ch = idx % (D / 8);
             uint2 h, l, m;
-            rotate_split8(r.raw[it], r.cs[it], h, l, m);
+            rotate_split8(r.raw[i], r.cs[i], h, l, m);
             char* p = lds + row * kRow + 8 * ch;
             *reinterpret_cast<uint2*>(p) = h;
             *reinterpret_cast<uint2*>(p + kPlane) = l;
@@ -409,8 +471,7 @@ struct I16QK {
     }
 
     // Exact int32 scores S^T for key block kb: 2^14 hh + 2^7 (mm - hh - ll) + ll.
-    __device__ static __forceinline__ void qk_i32(const char* lds, int kb, const Q& q, int (&s)[16], int lq,
-                                                  int lh) {
+    __device__ static __forceinline__ void qk_i32(const char* lds, int kb, const Q& q, int* s, int lq, int lh) {
         const char* row = lds + (32 * kb + lq) * kRow + 16 * lh;
         i32x16 hh = {}, ll = {}, mm = {};
 #pragma unroll
@@ -430,7 +491,8 @@ struct I16QK {
         }
     }
 
-    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float (&s)[16], int lq, int lh) {
+    // Logits (log2 units): float(score) * scale.
+    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh) {
         int si[16];
         qk_i32(lds, kb, q, si, lq, lh);
 #pragma unroll
@@ -438,123 +500,299 @@ struct I16QK {
     }
 };
 
+// ------------------------------------------------ balanced staging for 8 waves
+
+// With 512 threads every thread stages the same amount of a 64-key tile, so
+// no wave waits at the tile barrier for another wave's extra staging work:
+//  * K: thread (row r = tid/8, segment g = tid%8) rotates elements
+//    [g D/8, (g+1) D/8) of key row r, in granules of 4 elements (2 pairs);
+//  * V: thread (pair kp = tid%32, group dg = tid/32) converts dims
+//    [dg D/16, (dg+1) D/16) of keys 2kp and 2kp+1; each dim gives one
+//    (key, key+1) f16 pair of V^T.
+// The LDS layouts are those of Bf16QK (K' rows) and VStage (V^T rows, key
+// quads in the order 0,2,1,3 of each 16-key group).
+template <int D, int NT>
+struct Bf16Stage8 : Bf16QK<D, NT> {
+    static_assert(NT == 512, "one K unit per thread needs 512 threads");
+    using Base = Bf16QK<D, NT>;
+    using typename Base::KPtr;
+    static constexpr int kGran = D / 32;  // granules of 4 elements per thread
+    struct KRegs {
+        uint2 raw[kGran];
+        float4 cs[kGran];
+    };
+    template <bool CLAMP>
+    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
+        const int tid = threadIdx.x % NT;
+        int row = tid >> 3;
+        const int e0 = (tid & 7) * (D / 8);
+        if (CLAMP) row = min(row, p.S - 1 - tile * BN);
+        const char* kb = p.k.base + static_cast<size_t>(tile * BN) * p.k.stride;
+        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
+#pragma unroll
+        for (int i = 0; i < kGran; ++i) {
+            r.raw[i] = *reinterpret_cast<const uint2*>(kb + row * p.k.stride + 2 * (e0 + 4 * i));
+            r.cs[i] = ld16f(tb, (row * D + e0 + 4 * i) * 4);
+        }
+    }
+    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
+        const int tid = threadIdx.x % NT;
+        const int row = tid >> 3;
+        const int e0 = (tid & 7) * (D / 8);
+        _Float16* kl = reinterpret_cast<_Float16*>(lds) + row * Base::kStride + e0;
+#pragma unroll
+        for (int i = 0; i < kGran; ++i) {
+            const uint32_t w[2] = {r.raw[i].x, r.raw[i].y};
+            const float cs[4] = {r.cs[i].x, r.cs[i].y, r.cs[i].z, r.cs[i].w};
+            uint32_t o[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float x = bf_lo(w[j]), y = bf_hi(w[j]);
+                const float c = cs[2 * j], sn = cs[2 * j + 1];
+                o[j] = pack_h2(fmaf(x, c, -y * sn), fmaf(x, sn, y * c));
+            }
+            *reinterpret_cast<uint2*>(kl + 4 * i) = make_uint2(o[0], o[1]);
+        }
+    }
+};
+
+template <int D, int NT>
+struct VStage8 : VStage<D, NT> {
+    static_assert(NT == 512, "one V unit per thread needs 512 threads");
+    using Base = VStage<D, NT>;
+    static constexpr int kDims = D / 16;   // dims per thread
+    static constexpr int kWords = D / 32;  // dwords per key
+    struct Regs {
+        uint32_t w[2][kWords];
+    };
+    template <bool CLAMP>
+    __device__ static __forceinline__ void load(const Rows& p, int S, int tile, Regs& r) {
+        const int tid = threadIdx.x % NT;
+        const int kp = tid & 31, dg = tid >> 5;
+        const char* vb = p.base + static_cast<size_t>(tile * BN) * p.stride;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            int row = 2 * kp + kk;
+            if (CLAMP) row = min(row, S - 1 - tile * BN);
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(vb + row * p.stride + 2 * kDims * dg);
+#pragma unroll
+            for (int i = 0; i < kWords; ++i) r.w[kk][i] = src[i];
+        }
+    }
+    __device__ static __forceinline__ void commit(const Regs& r, _Float16* lds) {
+        const int tid = threadIdx.x % NT;
+        const int kp = tid & 31, dg = tid >> 5;
+        const int q = kp >> 1;  // key quad of keys 2kp, 2kp+1
+        const int pos = 4 * ((q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1)) + 2 * (kp & 1);
+#pragma unroll
+        for (int e = 0; e < kDims; ++e) {
+            const uint32_t w0 = r.w[0][e >> 1], w1 = r.w[1][e >> 1];
+            const float x0 = (e & 1) ? bf_hi(w0) : bf_lo(w0);
+            const float x1 = (e & 1) ? bf_hi(w1) : bf_lo(w1);
+            *reinterpret_cast<uint32_t*>(lds + (kDims * dg + e) * Base::kStride + pos) = pack_h2(x0, x1);
+        }
+    }
+};
+
 // ------------------------------------------------ fused kernel (f16 P.V)
 
-template <int D, template <int> class QK>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(RunArgs a, float logit_scale) {
-    using P = QK<D>;
-    using V = VStage<D>;
-    constexpr int kStage = P::kBytes + V::kBytes;
-    __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
+// One workgroup = NW waves x 32 query rows of one (batch, head).  Software
+// pipeline per 64-key tile t (LDS K' double buffer holds tiles t+1 / t+2,
+// V double buffer tiles t / t+1):
+//   issue global loads of K(t+2), V(t+1)
+//   softmax of S(t)                      (VALU, exp2)
+//   S(t+1) = K'(t+1) Q'^T                (MFMA, independent of the softmax)
+//   O^T += V^T(t) P~(t)^T                (MFMA)
+//   rotate K(t+2) -> LDS, convert V(t+1) -> LDS
+//   barrier
+// so the matrix cores have independent work queued while the vector unit
+// runs the softmax and the staging.  Tiles every query of the workgroup sees
+// in full run a branch-free copy of the step (no masks, no clamps).
+template <int D, template <int, int> class QKT, template <int, int> class VST, int NW>
+struct FusedAttn {
+    static constexpr int NT = 64 * NW;
+    static constexpr int BMW = 32 * NW;
+    using P = QKT<D, NT>;
+    using V = VST<D, NT>;
+    static constexpr int kLds = 2 * P::kBytes + 2 * V::kBytes;
 
+    char* lds;
     Ctx c;
-    if (!make_ctx(a, c)) {
-        zero_rows<D>(a, c);
-        return;
-    }
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int lq = lane & 31, lh = lane >> 5;
-    const int qw0 = c.q0 + 32 * w;  // this wave's first query row
-    const int n_tiles = (min(c.q0 + BM, c.S) + BN - 1) / BN;
-
+    int lq, lh, qw0, n_tiles;
+    typename P::KPtr kp;
+    Rows vp;
     typename P::KRegs kr;
     typename V::Regs vr;
-    P::load_k(a, c, 0, kr);
-    V::load(a, c, 0, vr);
-
     typename P::Q q;
-    P::load_q(a, c, qw0 + lq, logit_scale, q);
-
-    P::commit_k(kr, lds);
-    V::commit(vr, reinterpret_cast<_Float16*>(lds + P::kBytes));
-    __syncthreads();
-
     f32x16 o[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    float m_run = kNegInf, l_run = 0.f;
-    const uint32_t ones = pack_h2(1.f, 1.f);
+    float m_run, l_a, l_b;
 
-    for (int t = 0; t < n_tiles; ++t) {
-        const bool more = t + 1 < n_tiles;
-        if (more) {
-            P::load_k(a, c, t + 1, kr);
-            V::load(a, c, t + 1, vr);
-        }
-        const char* kbuf = lds + (t & 1) * kStage;
-        const _Float16* vbuf = reinterpret_cast<const _Float16*>(kbuf + P::kBytes);
-
+    __device__ __forceinline__ char* kbuf(int t) const { return lds + (t & 1) * P::kBytes; }
+    __device__ __forceinline__ _Float16* vbuf(int t) const {
+        return reinterpret_cast<_Float16*>(lds + 2 * P::kBytes + (t & 1) * V::kBytes);
+    }
+    // Active 32-key blocks of tile t for this wave (a prefix of {0, 1}); wave-uniform.
+    __device__ __forceinline__ int nact(int t) const {
+        if (qw0 >= c.S) return 0;
         const int kt0 = t * BN;
-        int nact = kt0 + 32 <= qw0 + 31 ? 2 : (kt0 <= qw0 + 31 ? 1 : 0);
-        if (qw0 >= c.S) nact = 0;
-        if (nact > 0) {
-            float s[2][16];
-            P::qk(kbuf, 0, q, s[0], lq, lh);
-            if (nact > 1) P::qk(kbuf, 1, q, s[1], lq, lh);
+        return kt0 + 32 <= qw0 + 31 ? 2 : (kt0 <= qw0 + 31 ? 1 : 0);
+    }
+
+    // Two sequential guards (not if / else-if), so the compiler cannot merge
+    // the two blocks' stores through a pointer select that would push the
+    // score array out of registers.
+    template <bool FULL>
+    __device__ __forceinline__ void qk_tile(int t, float* s) const {
+        const int na = FULL ? 2 : nact(t);
+        if (na >= 1) P::qk(kbuf(t), 0, q, s, lq, lh);
+        if (na == 2) P::qk(kbuf(t), 1, q, s + 16, lq, lh);
+    }
+
+    template <bool FULL>
+    __device__ __forceinline__ void softmax(int t, int na, float* s, uint32_t* pk) {
+        if (!FULL) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const int k0 = kt0 + 32 * kb;
-                if (kb < nact && k0 + 31 > qw0) {
+                const int k0 = t * BN + 32 * kb;
+                if (kb < na && k0 + 31 > qw0) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
-                        if (k0 + acc_row(v, lh) > qw0 + lq) s[kb][v] = kNegInf;
+                        if (k0 + acc_row(v, lh) > qw0 + lq) s[16 * kb + v] = kNegInf;
                 }
             }
-            float mx = kNegInf;
+        }
+        float mx = kNegInf;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                if (kb < nact) {
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb < na) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-                }
-            mx = halves_max(mx);
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[16 * kb + v]);
+            }
+        mx = halves_max(mx);
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
             const float m_new = fmaxf(m_run, mx);
-            if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack)) {
-                const float alpha = fast_exp2(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_a *= alpha;
+            l_b *= alpha;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-            }
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        }
+        const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                if (kb < nact) {
-                    uint32_t pk[8];
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb < na) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        pk[j] = pack_h2(fast_exp2(s[kb][2 * j] - m_run), fast_exp2(s[kb][2 * j + 1] - m_run));
-                        l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[j]),
-                                                       __builtin_bit_cast(f16x2, ones), l_run, false);
-                    }
-#pragma unroll
-                    for (int k2 = 0; k2 < 2; ++k2) {
-                        const u32x4 b4 = {pk[4 * k2], pk[4 * k2 + 1], pk[4 * k2 + 2], pk[4 * k2 + 3]};
-                        V::pv(vbuf, 2 * kb + k2, __builtin_bit_cast(f16x8, b4), o, lq, lh);
-                    }
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t p = pack_h2(fast_exp2(s[16 * kb + 2 * j] - m_run),
+                                               fast_exp2(s[16 * kb + 2 * j + 1] - m_run));
+                    pk[8 * kb + j] = p;
+                    if (j & 1)
+                        l_b = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), ones, l_b, false);
+                    else
+                        l_a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), ones, l_a, false);
                 }
-        }
-        if (more) {
-            char* nbuf = lds + ((t + 1) & 1) * kStage;
-            P::commit_k(kr, nbuf);
-            V::commit(vr, reinterpret_cast<_Float16*>(nbuf + P::kBytes));
-        }
+            }
+    }
+
+    __device__ __forceinline__ void pv_tile(int t, int na, const uint32_t* pk) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb < na) {
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    const u32x4 b4 = {pk[8 * kb + 4 * k2], pk[8 * kb + 4 * k2 + 1], pk[8 * kb + 4 * k2 + 2],
+                                      pk[8 * kb + 4 * k2 + 3]};
+                    V::pv(vbuf(t), 2 * kb + k2, __builtin_bit_cast(f16x8, b4), o, lq, lh);
+                }
+            }
+    }
+
+    // One pipeline step for tile t; s holds S(t) on entry, sn receives S(t+1).
+    template <bool STEADY>
+    __device__ __forceinline__ void step(int t, float* s, float* sn) {
+        const bool ld_k = STEADY || t + 2 < n_tiles;
+        const bool ld_v = STEADY || t + 1 < n_tiles;
+        if (ld_k) P::template load_k<!STEADY>(kp, t + 2, kr);
+        if (ld_v) V::template load<!STEADY>(vp, c.S, t + 1, vr);
+        const int na = STEADY ? 2 : nact(t);
+        uint32_t pk[16];
+        if (na > 0) softmax<STEADY>(t, na, s, pk);
+        if (ld_v) qk_tile<STEADY>(t + 1, sn);
+        if (na > 0) pv_tile(t, na, pk);
+        if (ld_k) P::commit_k(kr, kbuf(t));
+        if (ld_v) V::commit(vr, vbuf(t + 1));
         __syncthreads();
     }
 
-    if (qw0 >= c.S) return;
-    const float inv = 1.0f / halves_sum(l_run);
-    const int qi = qw0 + lq;
-    if (qi < c.S) {
-        float* orow = a.out + q_index(a, c, qi, D);
+    __device__ __forceinline__ void run(const RunArgs& a, float logit_scale) {
+        const int lane = threadIdx.x & 63;
+        const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+        lq = lane & 31;
+        lh = lane >> 5;
+        qw0 = c.q0 + 32 * w;
+        n_tiles = (min(c.q0 + BMW, c.S) + BN - 1) / BN;
+        const int n_full = min(c.q0 / BN, n_tiles);  // tiles every query of the workgroup sees whole
+        kp = P::kptr(a, c);
+        vp = kv_rows(a, c, a.v, D, 2);
+
+        P::template load_k<true>(kp, 0, kr);
+        V::template load<true>(vp, c.S, 0, vr);
+        P::load_q(a, c, qw0 + lq, logit_scale, q);
+        P::commit_k(kr, kbuf(0));
+        V::commit(vr, vbuf(0));
+        if (n_tiles > 1) {
+            P::template load_k<true>(kp, 1, kr);
+            P::commit_k(kr, kbuf(1));
+        }
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+        m_run = kNegInf;
+        l_a = 0.f;
+        l_b = 0.f;
+        __syncthreads();
+        float sa[32], sb[32];
+        qk_tile<false>(0, sa);
+        __syncthreads();  // every wave has read K'(0) before step 0 overwrites that buffer
+
+        int t = 0;
+        for (; t + 2 < n_full; t += 2) {
+            step<true>(t, sa, sb);
+            step<true>(t + 1, sb, sa);
+        }
+        for (; t < n_tiles; t += 2) {
+            step<false>(t, sa, sb);
+            if (t + 1 < n_tiles) step<false>(t + 1, sb, sa);
+        }
+
+        if (qw0 >= c.S) return;
+        const float inv = 1.0f / halves_sum(l_a + l_b);
+        const int qi = qw0 + lq;
+        if (qi < c.S) {
+            float* orow = a.out + q_index(a, c, qi, D);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 val = make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
-                                               o[db][4 * g + 3] * inv);
-                *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * lh) = val;
-            }
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 val = make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
+                                                   o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                    *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * lh) = val;
+                }
+        }
     }
+};
+
+template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, int MINB>
+__global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, float logit_scale) {
+    using K = FusedAttn<D, QKT, VST, NW>;
+    __shared__ __attribute__((aligned(16))) char lds[K::kLds];
+    K k;
+    k.lds = lds;
+    if (!make_ctx<K::BMW>(a, k.c)) {
+        zero_rows<D, K::BMW, K::NT>(a, k.c);
+        return;
+    }
+    k.run(a, logit_scale);
 }
 
 // ------------------------------------------------ fp32 kernel (fp32 matrix cores)
@@ -566,8 +804,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(RunArgs a, float
     __shared__ __attribute__((aligned(16))) float vs_[BN * kStride];
 
     Ctx c;
-    if (!make_ctx(a, c)) {
-        zero_rows<D>(a, c);
+    if (!make_ctx<BM>(a, c)) {
+        zero_rows<D, BM, kThreads>(a, c);
         return;
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -701,17 +939,17 @@ __global__ __launch_bounds__(kThreads) void debug_rope_i16_kernel(RunArgs a, int
     }
     const int x = src[2 * pair], y = src[2 * pair + 1];
     const int16_t* t = a.rope_q14 + static_cast<size_t>(off + i) * D + 2 * k;
-    dst[2 * pair] = static_cast<int16_t>(I16QK<D>::rot_x(x, y, t[0], t[1]));
-    dst[2 * pair + 1] = static_cast<int16_t>(I16QK<D>::rot_y(x, y, t[0], t[1]));
+    dst[2 * pair] = static_cast<int16_t>(I16QK<D, kThreads>::rot_x(x, y, t[0], t[1]));
+    dst[2 * pair + 1] = static_cast<int16_t>(I16QK<D, kThreads>::rot_y(x, y, t[0], t[1]));
 }
 
 // Full (unmasked) int32 score matrix through the same staging and MFMA code.
 template <int D>
 __global__ __launch_bounds__(kThreads) void debug_scores_i32_kernel(RunArgs a, int32_t* dst) {
-    using P = I16QK<D>;
+    using P = I16QK<D, kThreads>;
     __shared__ __attribute__((aligned(16))) char lds[P::kBytes];
     Ctx c;
-    if (!make_ctx(a, c)) {
+    if (!make_ctx<BM>(a, c)) {
         if (threadIdx.x == 0) atomicOr(a.status, 1);
         return;
     }
@@ -721,15 +959,17 @@ __global__ __launch_bounds__(kThreads) void debug_scores_i32_kernel(RunArgs a, i
     typename P::Q q;
     P::load_q(a, c, qw0 + lq, 1.0f, q);
     const int n_tiles = (c.S + BN - 1) / BN;
+    const typename P::KPtr kp = P::kptr(a, c);
     for (int t = 0; t < n_tiles; ++t) {
         typename P::KRegs kr;
-        P::load_k(a, c, t, kr);
+        P::template load_k<true>(kp, t, kr);
         __syncthreads();
         P::commit_k(kr, lds);
         __syncthreads();
+        // Every lane takes part in the MFMAs (a lane's A operand feeds the other
+        // lanes' results); only the stores are limited to real queries and keys.
         const int qi = qw0 + lq;
-        if (qi >= c.S) continue;
-        int32_t* row = dst + ((static_cast<size_t>(c.b) * a.n_heads + c.hq) * c.S + qi) * c.S;
+        int32_t* row = dst + ((static_cast<size_t>(c.b) * a.n_heads + c.hq) * c.S + min(qi, c.S - 1)) * c.S;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             int s[16];
@@ -737,7 +977,7 @@ __global__ __launch_bounds__(kThreads) void debug_scores_i32_kernel(RunArgs a, i
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int key = t * BN + 32 * kb + acc_row(v, lh);
-                if (key < c.S) row[key] = s[v];
+                if (qi < c.S && key < c.S) row[key] = s[v];
             }
         }
     }
@@ -745,24 +985,34 @@ __global__ __launch_bounds__(kThreads) void debug_scores_i32_kernel(RunArgs a, i
 
 // ------------------------------------------------ launch helpers
 
-dim3 grid_for(const RunArgs& a) {
-    const int n_qblocks = (a.seq_len + BM - 1) / BM;
+dim3 grid_for(const RunArgs& a, int bm) {
+    const int n_qblocks = (a.seq_len + bm - 1) / bm;
     return dim3(static_cast<unsigned>(n_qblocks) * a.batch * a.n_heads);
 }
 
+// 256-row eight-wave workgroups when they still give every CU work; otherwise
+// (short sequences, few heads) 128-row four-wave workgroups for parallelism.
 template <int D>
 hipError_t launch_bf16_d(const RunArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16QK>), grid_for(a), dim3(kThreads), 0, s, a, a.score_scale * kLog2e);
+    const long long wgs256 = static_cast<long long>((a.seq_len + 255) / 256) * a.batch * a.n_heads;
+    if (wgs256 >= 256) {
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1>), grid_for(a, 256), dim3(512), 0, s, a,
+                           a.score_scale * kLog2e);
+    } else {
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16QK, VStage, 4, 2>), grid_for(a, 128), dim3(256), 0, s, a,
+                           a.score_scale * kLog2e);
+    }
     return hipGetLastError();
 }
 template <int D>
 hipError_t launch_i16_d(const RunArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, I16QK>), grid_for(a), dim3(kThreads), 0, s, a, a.score_scale * kLog2e);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, I16QK, VStage, 4, 1>), grid_for(a, 128), dim3(256), 0, s, a,
+                       a.score_scale * kLog2e);
     return hipGetLastError();
 }
 template <int D>
 hipError_t launch_f32_d(const RunArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), grid_for(a), dim3(kThreads), 0, s, a, a.score_scale * kLog2e);
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), grid_for(a, BM), dim3(kThreads), 0, s, a, a.score_scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -792,7 +1042,7 @@ hipError_t launch_rope_d(const RunArgs& a, int n_heads_x, int16_t* dst, hipStrea
 }
 template <int D>
 hipError_t launch_scores_d(const RunArgs& a, int32_t* dst, hipStream_t s) {
-    hipLaunchKernelGGL((debug_scores_i32_kernel<D>), grid_for(a), dim3(kThreads), 0, s, a, dst);
+    hipLaunchKernelGGL((debug_scores_i32_kernel<D>), grid_for(a, BM), dim3(kThreads), 0, s, a, dst);
     return hipGetLastError();
 }
 }  // namespace

@@ -46,11 +46,35 @@ def test_float_small_full_compare(case):
     name, B, Hq, Hkv, S, D, dt, theta, offs = case
     announce(name)
     max_seq = S + (max(offs) if offs else 0)
-    w = synth.Workload(name, B, Hq, Hkv, S, D, dt, theta, seed=hash(name) % 10000, max_seq=max_seq)
+    w = synth.Workload(name, B, Hq, Hkv, S, D, dt, theta, seed=sum(map(ord, name)), max_seq=max_seq)
     q, k, v = synth.make_inputs(w)
     got = run_gpu(w, q, k, v, pos_offsets=offs)
     want = oracle_full(w, q, k, v, pos_offsets=offs)
     mx, mean = assert_close(got.numpy(), want, dt)
+    announce(name, f"max {mx:.2e} mean {mean:.2e}")
+
+
+# Shapes with at least 256 workgroups of 256 query rows run the eight-wave
+# ping-pong kernel; the cases above run the four-wave kernel.
+PINGPONG_CASES = [
+    # name, batch, Hq, Hkv, S, D, theta, offsets
+    ("pp_d96_ragged_gqa", 2, 32, 16, 1100, 96, 1e4, [0, 37]),
+    ("pp_d128_ragged", 2, 32, 32, 1030, 128, 1e6, None),
+    ("pp_d64_exact", 1, 64, 8, 1024, 64, 1e4, [5]),
+]
+
+
+@pytest.mark.parametrize("case", PINGPONG_CASES, ids=[c[0] for c in PINGPONG_CASES])
+def test_pingpong_shapes_full_compare(case):
+    name, B, Hq, Hkv, S, D, theta, offs = case
+    assert B * Hq * ((S + 255) // 256) >= 256
+    announce(name)
+    max_seq = S + (max(offs) if offs else 0)
+    w = synth.Workload(name, B, Hq, Hkv, S, D, "bf16", theta, seed=sum(map(ord, name)), max_seq=max_seq)
+    q, k, v = synth.make_inputs(w)
+    got = run_gpu(w, q, k, v, pos_offsets=offs)
+    want = oracle_full(w, q, k, v, pos_offsets=offs)
+    mx, mean = assert_close(got.numpy(), want, "bf16")
     announce(name, f"max {mx:.2e} mean {mean:.2e}")
 
 
