@@ -19,12 +19,16 @@ Pages cited (by title and section):
   attention as blocked online softmax (QK, online softmax, PV in one pass).
 * the XNet-DNN article (www.szyisi.cn/article/817147.html), §三.3
   FlashAttention-2 -- online softmax, deferred rescale.
+* "手写内核实现6倍prefill加速" §2.2 and §3.2 again for the KV cache: new
+  tokens' K/V copied into free slots, an index map from logical position to
+  physical slot (``kv_cache.py``).
 
 The blocked online softmax of those pages reaches, in exact arithmetic, the
 plain causal softmax-attention result; so this oracle is that plain
 definition: explicit RoPE, the full causal score matrix, a two-pass softmax.
 
-Parity pins (tests/test_oracle_pins.py) cover every function here; none is
+Parity pins (tests/test_oracle_pins.py, tests/test_oracle_cache_pins.py)
+cover every function here; none is
 "parity unpinned".  Two *inputs* are readings rather than derivations and are
 documented as such with the workloads: the int16 ``score_scale`` and the
 per-head scale recipe of the long-prompt workload.
@@ -37,6 +41,15 @@ from .attention import (
     causal_probs,
     attention,
     attention_rows,
+)
+from .kv_cache import (
+    ring_index_map,
+    paged_index_map,
+    kv_cache_update,
+    gather_logical,
+    attention_cached,
+    attention_cached_rows,
+    attention_i16_cached,
 )
 from .fixed_point import (
     rope_table_q14,
@@ -58,4 +71,11 @@ __all__ = [
     "scores_i32",
     "attention_i16",
     "attention_i16_rows",
+    "ring_index_map",
+    "paged_index_map",
+    "kv_cache_update",
+    "gather_logical",
+    "attention_cached",
+    "attention_cached_rows",
+    "attention_i16_cached",
 ]
