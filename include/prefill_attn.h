@@ -63,7 +63,8 @@ enum prefill_attn_status {
     PA_ENOMEM = -2,  /* device or host allocation failed (init only) */
     PA_EDEVICE = -3, /* no device, or the current device is not gfx950 */
     PA_ELAUNCH = -4, /* the HIP runtime rejected a launch or a copy */
-    PA_ERANGE = -5   /* a run saw pos_offsets[b] < 0 or pos_offsets[b] + seq_len > max_seq */
+    PA_ERANGE = -5   /* a run saw pos_offsets[b] < 0 or pos_offsets[b] + seq_len > max_seq (or, for the
+                        cache calls, beyond map_stride, or a map entry outside the cache) */
 };
 
 /*
@@ -102,8 +103,70 @@ int prefill_attn_run(const prefill_attn* h, int in_dtype, int batch, int seq_len
                      void* stream);
 
 /*
+ * KV-prefix (chunked) prefill against a KV cache.
+ *
+ * Sources: the page titled "手写内核实现6倍prefill加速", §2.2 (the cache-update
+ * kernel copies only the K/V of the new tokens and leaves older entries in
+ * place) and §3.2 (ring KV cache: K/V stored wherever there is room, with an
+ * index map holding one physical offset per logical position, so attention
+ * still reads the keys in logical order); the 2kiu.com retelling, §3.4 (a
+ * ring of fixed slots indexed with a wrap-around).
+ *
+ * A cache is a pair of device tensors K_cache, V_cache [n_slots][n_kv_heads][head_dim]
+ * owned by the caller (element type as for prefill_attn_run: f32, bf16, or
+ * int16 K with bf16 V).  kv_map is a device int32 [batch][map_stride]:
+ * kv_map[b*map_stride + j] is the slot holding logical position j of
+ * sequence b.  pos_offsets[b] (NULL = all 0) is the number of positions the
+ * cache already holds for sequence b, so the chunk's token i has logical
+ * position and RoPE position pos_offsets[b] + i.
+ *
+ * prefill_attn_kv_cache_update: copies K_new, V_new [batch][seq_len][n_kv_heads][head_dim]
+ *   (token i of sequence b) into slot kv_map[b*map_stride + pos_offsets[b] + i] of
+ *   the caches.  Nothing else is written.  The slots the new tokens map to must be
+ *   distinct (otherwise which write lands is unspecified).
+ * prefill_attn_run_cached: for the chunk's queries Q [batch][seq_len][n_heads][head_dim],
+ *     O[b,i,h,:] = sum_{j <= P+i} softmax_j( RoPE_{P+i}(Q[b,i,h]) . RoPE_j(Kc[map(b,j), kvh(h)]) * scale ) Vc[map(b,j), kvh(h)]
+ *   with P = pos_offsets[b] and map(b,j) = kv_map[b*map_stride + j]: keys are read
+ *   through the index map in logical order and rotated at their logical position,
+ *   inside the same fused kernel as prefill_attn_run.  The chunk's own K/V must
+ *   already be in the cache (call prefill_attn_kv_cache_update first, on the same
+ *   stream).  With pos_offsets all 0 and the identity map this is prefill_attn_run.
+ * Both: asynchronous on `stream`, no allocation.  PA_EINVAL for a bad shape or
+ *   pointer: n_slots < 1, map_stride < max(1, seq_len), a cache larger than
+ *   2^32 - 1 bytes, NULL or misaligned pointers (caches, Q, K_new, V_new, out 16-byte,
+ *   kv_map and pos_offsets 4-byte aligned), an unknown dtype.  On the device, a
+ *   sequence with pos_offsets[b] < 0 or pos_offsets[b] + seq_len > map_stride
+ *   (for the run also > max_seq) is skipped (run: O = 0) and a map entry outside
+ *   [0, n_slots) is read as slot 0 (update: skipped); both set the status word
+ *   (PA_ERANGE from prefill_attn_status).  The caller owns caches, map and offsets.
+ */
+int prefill_attn_kv_cache_update(const prefill_attn* h, int in_dtype, int batch, int seq_len,
+                                 const void* k_new, const void* v_new, const int32_t* pos_offsets,
+                                 const int32_t* kv_map, int map_stride,
+                                 void* k_cache, void* v_cache, int n_slots, void* stream);
+int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int batch, int seq_len,
+                            const void* q, const void* k_cache, const void* v_cache, int n_slots,
+                            const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
+                            float* out, float score_scale, void* stream);
+
+/*
+ * Host-only index-map builders (caller-owned host arrays; copy the result to the
+ * device row of the sequence).
+ *   prefill_attn_ring_map:  map[j] = (start + j) mod n_slots, j < count (a ring of
+ *     n_slots slots whose oldest live position sits at `start`); needs n_slots >= 1,
+ *     0 <= start < n_slots, count >= 0.
+ *   prefill_attn_paged_map: map[j] = block_table[j / block_size] * block_size + j % block_size,
+ *     j < count (the cache cut into blocks of block_size slots, block_table[n] the
+ *     physical block of logical block n); needs block_size >= 1, n_blocks blocks
+ *     covering count positions, non-negative blocks and slots below 2^31.
+ */
+int prefill_attn_ring_map(int n_slots, int start, int count, int32_t* map);
+int prefill_attn_paged_map(const int32_t* block_table, int n_blocks, int block_size, int count, int32_t* map);
+
+/*
  * Synchronise `stream`, then report and clear the status word: PA_ERANGE if any
- * run since the last call saw an out-of-range position, else PA_OK.
+ * call since the last status call saw an out-of-range position, map row or
+ * slot, else PA_OK.
  */
 int prefill_attn_status(prefill_attn* h, void* stream);
 

@@ -24,6 +24,7 @@ __all__ = [
     "prefill_attn_init", "prefill_attn_run", "prefill_attn_status", "prefill_attn_destroy",
     "prefill_attn_strerror", "prefill_attn_rope_table_f32", "prefill_attn_rope_table_q14",
     "prefill_attn_debug_rope_i16", "prefill_attn_debug_scores_i32",
+    "prefill_attn_kv_cache_update", "prefill_attn_run_cached", "prefill_attn_ring_map", "prefill_attn_paged_map",
     "PrefillAttention", "EXPORTED_SYMBOLS",
 ]
 
@@ -45,6 +46,10 @@ _SIGNATURES = {
     "prefill_attn_rope_table_q14": (_I, [_I, _I, ctypes.c_double, _P]),
     "prefill_attn_debug_rope_i16": (_I, [_P, _I, _I, _P, _I, _P, _P, _P]),
     "prefill_attn_debug_scores_i32": (_I, [_P, _I, _I, _P, _P, _P, _P, _P]),
+    "prefill_attn_kv_cache_update": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _I, _P]),
+    "prefill_attn_run_cached": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _P]),
+    "prefill_attn_ring_map": (_I, [_I, _I, _I, _P]),
+    "prefill_attn_paged_map": (_I, [_P, _I, _I, _I, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -182,6 +187,41 @@ def prefill_attn_debug_scores_i32(handle, batch, seq_len, q, k, pos_offsets, sco
            "prefill_attn_debug_scores_i32")
 
 
+def prefill_attn_kv_cache_update(handle, in_dtype, batch, seq_len, k_new, v_new, pos_offsets, kv_map, map_stride,
+                                 k_cache, v_cache, n_slots, stream=None):
+    """Copy the new tokens' K/V into their cache slots (see the header)."""
+    _check(load_library().prefill_attn_kv_cache_update(handle, in_dtype, batch, seq_len, _ptr(k_new), _ptr(v_new),
+                                                       _ptr(pos_offsets), _ptr(kv_map), map_stride, _ptr(k_cache),
+                                                       _ptr(v_cache), n_slots, _stream(stream)),
+           "prefill_attn_kv_cache_update")
+
+
+def prefill_attn_run_cached(handle, in_dtype, batch, seq_len, q, k_cache, v_cache, n_slots, kv_map, map_stride,
+                            pos_offsets, out, score_scale=0.0, stream=None):
+    """Enqueue one cached (chunked) prefill pass (see the header)."""
+    _check(load_library().prefill_attn_run_cached(handle, in_dtype, batch, seq_len, _ptr(q), _ptr(k_cache),
+                                                  _ptr(v_cache), n_slots, _ptr(kv_map), map_stride,
+                                                  _ptr(pos_offsets), _ptr(out), float(score_scale),
+                                                  _stream(stream)),
+           "prefill_attn_run_cached")
+
+
+def prefill_attn_ring_map(n_slots, start, count):
+    """Host int32 map[j] = (start + j) mod n_slots, j < count."""
+    out = np.empty(max(count, 1), dtype=np.int32)
+    _check(load_library().prefill_attn_ring_map(n_slots, start, count, out.ctypes.data), "prefill_attn_ring_map")
+    return out[:count]
+
+
+def prefill_attn_paged_map(block_table, block_size, count):
+    """Host int32 map[j] = block_table[j // block_size] * block_size + j % block_size."""
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    out = np.empty(max(count, 1), dtype=np.int32)
+    _check(load_library().prefill_attn_paged_map(bt.ctypes.data if bt.size else None, bt.size, block_size, count,
+                                                 out.ctypes.data), "prefill_attn_paged_map")
+    return out[:count]
+
+
 # ------------------------------------------------------------- tensor helper
 
 _DTYPES = {torch.float32: PA_IN_F32, torch.bfloat16: PA_IN_BF16, torch.int16: PA_IN_I16}
@@ -241,3 +281,55 @@ class PrefillAttention:
 
     def status(self, stream=None):
         return prefill_attn_status(self.handle, stream)
+
+    # ---- KV cache (chunked prefill)
+
+    def _check_cache(self, k_cache, v_cache, kv_map, dt, B):
+        if k_cache.dim() != 3 or tuple(k_cache.shape[1:]) != (self.n_kv_heads, self.head_dim):
+            raise ValueError("caches must be [n_slots][n_kv_heads][head_dim]")
+        if tuple(v_cache.shape) != tuple(k_cache.shape):
+            raise ValueError("k_cache and v_cache must have the same shape")
+        if k_cache.dtype != {PA_IN_F32: torch.float32, PA_IN_BF16: torch.bfloat16, PA_IN_I16: torch.int16}[dt] or \
+                v_cache.dtype != (torch.bfloat16 if dt == PA_IN_I16 else k_cache.dtype):
+            raise TypeError("cache dtypes must match the inputs (int16 K with bfloat16 V for the int16 variant)")
+        if kv_map.dtype != torch.int32 or kv_map.dim() != 2 or kv_map.shape[0] != B:
+            raise ValueError("kv_map must be int32 [batch][map_stride]")
+        for t in (k_cache, v_cache, kv_map):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("caches and kv_map must be contiguous device tensors")
+        return k_cache.shape[0], kv_map.shape[1]
+
+    def kv_cache_update(self, k_new, v_new, k_cache, v_cache, kv_map, pos_offsets=None, stream=None):
+        """Write k_new/v_new [B][S][Hkv][D] to slots kv_map[b][pos_offsets[b] + i]."""
+        dt = _DTYPES.get(k_new.dtype)
+        if dt is None:
+            raise TypeError(f"unsupported dtype {k_new.dtype}")
+        B, S = k_new.shape[:2]
+        if tuple(k_new.shape) != (B, S, self.n_kv_heads, self.head_dim) or v_new.shape != k_new.shape:
+            raise ValueError("k_new/v_new must be [B][S][n_kv_heads][head_dim]")
+        if not (k_new.is_contiguous() and v_new.is_contiguous()):
+            raise ValueError("k_new/v_new must be contiguous")
+        n_slots, stride = self._check_cache(k_cache, v_cache, kv_map, dt, B)
+        prefill_attn_kv_cache_update(self.handle, dt, B, S, k_new, v_new, pos_offsets, kv_map, stride, k_cache,
+                                     v_cache, n_slots, stream)
+
+    def run_cached(self, q, k_cache, v_cache, kv_map, pos_offsets=None, score_scale=0.0, out=None, stream=None):
+        """Chunked prefill: queries q [B][S][Hq][D] at positions pos_offsets[b] + i
+        against the cached logical keys 0 .. pos_offsets[b] + i.  Returns O (float32)."""
+        dt = _DTYPES.get(q.dtype)
+        if dt is None:
+            raise TypeError(f"unsupported q dtype {q.dtype}")
+        B, S, Hq, D = q.shape
+        if Hq != self.n_heads or D != self.head_dim or not q.is_cuda or not q.is_contiguous():
+            raise ValueError("q must be a contiguous device tensor [B][S][n_heads][head_dim]")
+        n_slots, stride = self._check_cache(k_cache, v_cache, kv_map, dt, B)
+        if pos_offsets is not None and (pos_offsets.dtype != torch.int32 or pos_offsets.numel() != B
+                                        or not pos_offsets.is_cuda):
+            raise ValueError("pos_offsets must be a device int32 tensor with one entry per batch element")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        elif out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+            raise ValueError("out must be contiguous float32 [B][S][n_heads][head_dim]")
+        prefill_attn_run_cached(self.handle, dt, B, S, q, k_cache, v_cache, n_slots, kv_map, stride, pos_offsets,
+                                out, score_scale, stream)
+        return out

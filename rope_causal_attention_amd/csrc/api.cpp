@@ -139,6 +139,104 @@ extern "C" int prefill_attn_run(const prefill_attn* h, int in_dtype, int batch, 
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
+namespace {
+
+int elem_bytes(int in_dtype) {
+    switch (in_dtype) {
+        case PA_IN_F32: return 4;
+        case PA_IN_BF16: return 2;
+        case PA_IN_I16: return 2;  // int16 K, bf16 V
+        default: return 0;
+    }
+}
+
+// Cache-shape checks shared by the cache update and the cached run.
+int check_cache(const prefill_attn* h, int el, int seq_len, int n_slots, const int32_t* kv_map, int map_stride,
+                const void* k_cache, const void* v_cache) {
+    if (el == 0 || n_slots < 1 || map_stride < 1 || map_stride < seq_len) return PA_EINVAL;
+    // slot offsets are 32-bit byte offsets inside the kernels
+    const unsigned long long bytes = static_cast<unsigned long long>(n_slots) * h->n_kv_heads * h->head_dim * el;
+    if (bytes > 0xffffffffULL) return PA_EINVAL;
+    if (!kv_map || !aligned4(kv_map)) return PA_EINVAL;
+    if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache)) return PA_EINVAL;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int prefill_attn_kv_cache_update(const prefill_attn* h, int in_dtype, int batch, int seq_len,
+                                            const void* k_new, const void* v_new, const int32_t* pos_offsets,
+                                            const int32_t* kv_map, int map_stride, void* k_cache, void* v_cache,
+                                            int n_slots, void* stream) {
+    pa::RunArgs a;
+    int rc = prepare(h, batch, seq_len, pos_offsets, a);
+    if (rc != PA_OK) return rc;
+    const int el = elem_bytes(in_dtype);
+    if (el == 0) return PA_EINVAL;
+    if (batch == 0 || seq_len == 0) return PA_OK;
+    rc = check_cache(h, el, seq_len, n_slots, kv_map, map_stride, k_cache, v_cache);
+    if (rc != PA_OK) return rc;
+    if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return PA_EINVAL;
+    a.k = k_new;
+    a.v = v_new;
+    a.kv_map = kv_map;
+    a.map_stride = map_stride;
+    a.n_slots = n_slots;
+    hipError_t e = pa::launch_kv_cache_update(h->head_dim, el, a, k_cache, v_cache, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+extern "C" int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int batch, int seq_len, const void* q,
+                                       const void* k_cache, const void* v_cache, int n_slots, const int32_t* kv_map,
+                                       int map_stride, const int32_t* pos_offsets, float* out, float score_scale,
+                                       void* stream) {
+    pa::RunArgs a;
+    int rc = prepare(h, batch, seq_len, pos_offsets, a);
+    if (rc != PA_OK) return rc;
+    const int el = elem_bytes(in_dtype);
+    if (el == 0 || !std::isfinite(score_scale)) return PA_EINVAL;
+    if (batch == 0 || seq_len == 0) return PA_OK;
+    rc = check_cache(h, el, seq_len, n_slots, kv_map, map_stride, k_cache, v_cache);
+    if (rc != PA_OK) return rc;
+    if (!q || !out || !aligned16(q) || !aligned16(out)) return PA_EINVAL;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.kv_map = kv_map;
+    a.map_stride = map_stride;
+    a.n_slots = n_slots;
+    a.score_scale = score_scale != 0.0f ? score_scale : 1.0f / std::sqrt(static_cast<float>(h->head_dim));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (in_dtype) {
+        case PA_IN_F32: e = pa::launch_attn_f32(h->head_dim, a, s); break;
+        case PA_IN_BF16: e = pa::launch_attn_bf16(h->head_dim, a, s); break;
+        default: e = pa::launch_attn_i16(h->head_dim, a, s); break;
+    }
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+extern "C" int prefill_attn_ring_map(int n_slots, int start, int count, int32_t* map) {
+    if (n_slots < 1 || start < 0 || start >= n_slots || count < 0 || (count > 0 && !map)) return PA_EINVAL;
+    for (int j = 0; j < count; ++j) map[j] = static_cast<int32_t>((static_cast<long long>(start) + j) % n_slots);
+    return PA_OK;
+}
+
+extern "C" int prefill_attn_paged_map(const int32_t* block_table, int n_blocks, int block_size, int count,
+                                      int32_t* map) {
+    if (block_size < 1 || count < 0 || n_blocks < 0) return PA_EINVAL;
+    if (count == 0) return PA_OK;
+    if (!block_table || !map || (count - 1) / block_size >= n_blocks) return PA_EINVAL;
+    for (int j = 0; j < count; ++j) {
+        const long long blk = block_table[j / block_size];
+        const long long slot = blk * block_size + j % block_size;
+        if (blk < 0 || slot > 0x7fffffffLL) return PA_EINVAL;
+        map[j] = static_cast<int32_t>(slot);
+    }
+    return PA_OK;
+}
+
 extern "C" int prefill_attn_status(prefill_attn* h, void* stream) {
     if (!h) return PA_EINVAL;
     if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ELAUNCH;
@@ -163,7 +261,7 @@ extern "C" const char* prefill_attn_strerror(int code) {
         case PA_ENOMEM: return "out of memory";
         case PA_EDEVICE: return "no usable gfx950 device";
         case PA_ELAUNCH: return "HIP runtime error";
-        case PA_ERANGE: return "position outside the RoPE table";
+        case PA_ERANGE: return "position outside the RoPE table or the index map, or a slot outside the cache";
         default: return "unknown status code";
     }
 }

@@ -77,6 +77,20 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// Rotated pair (x c - y s, x s + y c) packed as two fp16.  The products y s
+// and y c are rounded to fp32; each fused multiply-add then rounds once,
+// straight to fp16 (v_fma_mix with fp32 sources).  Spelled out so that every
+// copy of the staging code rounds K' the same way: left to itself the
+// compiler fuses the fp16 conversion into the FMA in some copies and not in
+// others, which would make K' depend on which pipeline step staged the tile.
+__device__ __forceinline__ uint32_t rot_pack_h2(float x, float y, float c, float s) {
+    const float ys = -y * s, yc = y * c;
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(c), "v"(ys));
+    asm("v_fma_mixhi_f16 %0, %1, %2, %3" : "+v"(r) : "v"(x), "v"(s), "v"(yc));
+    return r;
+}
+
 // Combine a per-lane value with the same lane of the other 32-lane half.
 __device__ __forceinline__ float halves_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -122,11 +136,18 @@ __device__ __forceinline__ BlockPos map_block(int n_qblocks, int batch, int n_he
     return {qb, bh / n_heads, bh % n_heads};
 }
 
+// Query i of the workgroup's (batch, head) has table position off + i.  Keys
+// are numbered in key space: key j has table position koff + j, the keys a
+// query i sees are j <= kshift + i, and there are NK = kshift + S keys.
+//  * plain prefill: the keys are the same S tokens, koff = off, kshift = 0;
+//  * cached prefill (MAPPED): the keys are logical positions 0 .. off + S - 1
+//    of the cache, koff = 0, kshift = off (the tokens cached before the chunk).
 struct Ctx {
     int b, hq, hkv, off, S, q0;
+    int koff, kshift, NK;
 };
 
-template <int BM>
+template <int BM, bool MAPPED>
 __device__ __forceinline__ bool make_ctx(const RunArgs& a, Ctx& c) {
     const int n_qblocks = (a.seq_len + BM - 1) / BM;
     const BlockPos bp = map_block(n_qblocks, a.batch, a.n_heads);
@@ -136,7 +157,11 @@ __device__ __forceinline__ bool make_ctx(const RunArgs& a, Ctx& c) {
     c.S = a.seq_len;
     c.q0 = bp.qb * BM;
     c.off = a.pos_offsets ? a.pos_offsets[bp.b] : 0;
-    return c.off >= 0 && static_cast<long long>(c.off) + a.seq_len <= a.max_seq;
+    c.koff = MAPPED ? 0 : c.off;
+    c.kshift = MAPPED ? c.off : 0;
+    c.NK = c.kshift + c.S;
+    const long long end = static_cast<long long>(c.off) + a.seq_len;
+    return c.off >= 0 && end <= a.max_seq && (!MAPPED || end <= a.map_stride);
 }
 
 __device__ __forceinline__ size_t q_index(const RunArgs& a, const Ctx& c, int i, int D) {
@@ -146,16 +171,45 @@ __device__ __forceinline__ size_t kv_index(const RunArgs& a, const Ctx& c, int j
     return ((static_cast<size_t>(c.b) * c.S + j) * a.n_kv_heads + c.hkv) * D;
 }
 
-// Rows of one (batch, head) of a [B][S][H][D] tensor: uniform base + 32-bit byte offsets.
+// Rows of one (batch, head): a uniform base plus 32-bit byte offsets.
+//  * plain: token j of a [B][S][H][D] tensor is at base + j * stride;
+//  * mapped (cached prefill): logical key j is in cache slot map[j], at
+//    base + map[j] * stride.  A slot outside [0, n_slots) reads slot 0 and
+//    sets the status word, so a bad map never reads outside the cache.
 struct Rows {
     const char* base;
-    uint32_t stride;  // bytes between consecutive tokens
+    uint32_t stride;     // bytes between consecutive tokens / slots
+    const int32_t* map;  // mapped only: this sequence's row of the index map
+    int n_slots;
+    int* status;
+
+    // Base of the 64-key tile `tile`, and the offset of its row `row`.
+    template <bool MAPPED>
+    __device__ __forceinline__ const char* tile_base(int tile) const {
+        return MAPPED ? base : base + static_cast<size_t>(tile * BN) * stride;
+    }
+    template <bool MAPPED>
+    __device__ __forceinline__ uint32_t row_off(int tile, int row) const {
+        if (!MAPPED) return static_cast<uint32_t>(row) * stride;
+        int slot = map[tile * BN + row];
+        if (static_cast<unsigned>(slot) >= static_cast<unsigned>(n_slots)) {
+            atomicOr(status, 1);
+            slot = 0;
+        }
+        return static_cast<uint32_t>(slot) * stride;
+    }
 };
+template <bool MAPPED>
 __device__ __forceinline__ Rows kv_rows(const RunArgs& a, const Ctx& c, const void* t, int D, int el) {
-    return {static_cast<const char*>(t) + kv_index(a, c, 0, D) * el, static_cast<uint32_t>(a.n_kv_heads * D * el)};
+    const uint32_t stride = static_cast<uint32_t>(a.n_kv_heads * D * el);
+    if (MAPPED)
+        return {static_cast<const char*>(t) + static_cast<size_t>(c.hkv) * D * el, stride,
+                a.kv_map + static_cast<size_t>(c.b) * a.map_stride, a.n_slots, a.status};
+    return {static_cast<const char*>(t) + kv_index(a, c, 0, D) * el, stride, nullptr, 0, nullptr};
 }
 __device__ __forceinline__ Rows q_rows(const RunArgs& a, const Ctx& c, const void* t, int D, int el) {
-    return {static_cast<const char*>(t) + q_index(a, c, 0, D) * el, static_cast<uint32_t>(a.n_heads * D * el)};
+    return {static_cast<const char*>(t) + q_index(a, c, 0, D) * el, static_cast<uint32_t>(a.n_heads * D * el),
+            nullptr, 0, nullptr};
 }
 
 // A batch element whose positions leave the tables: O = 0 and the status word is set.
@@ -191,9 +245,9 @@ struct VStage {
     __device__ static __forceinline__ bool has(int i) { return kItems % NT == 0 || static_cast<int>(threadIdx.x % NT) + NT * i < kItems; }
     // Loads are unconditional (surplus threads re-read the last item) so that no
     // branch separates a load from its use; only the commit is guarded.
-    template <bool CLAMP>
+    template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load(const Rows& p, int S, int tile, Regs& r) {
-        const char* vb = p.base + static_cast<size_t>(tile * BN) * p.stride;
+        const char* vb = p.tile_base<MAPPED>(tile);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int idx = min(static_cast<int>(threadIdx.x % NT) + NT * i, kItems - 1);
@@ -202,7 +256,7 @@ struct VStage {
             for (int rr = 0; rr < 4; ++rr) {
                 int row = 4 * kq + rr;
                 if (CLAMP) row = min(row, S - 1 - tile * BN);
-                r.raw[i][rr] = ld16(vb, row * p.stride + 16 * dc);
+                r.raw[i][rr] = ld16(vb, p.row_off<MAPPED>(tile, row) + 16 * dc);
             }
         }
     }
@@ -277,9 +331,10 @@ struct Bf16QK {
         return make_uint4(o[0], o[1], o[2], o[3]);
     }
 
+    template <bool MAPPED>
     __device__ static __forceinline__ KPtr kptr(const RunArgs& a, const Ctx& c) {
-        return {kv_rows(a, c, a.k, D, 2), reinterpret_cast<const char*>(a.rope_f32 + static_cast<size_t>(c.off) * D),
-                c.S};
+        return {kv_rows<MAPPED>(a, c, a.k, D, 2),
+                reinterpret_cast<const char*>(a.rope_f32 + static_cast<size_t>(c.koff) * D), c.NK};
     }
 
     __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
@@ -304,9 +359,9 @@ struct Bf16QK {
     __device__ static __forceinline__ bool has(int i) { return kChunks % NT == 0 || static_cast<int>(threadIdx.x % NT) + NT * i < kChunks; }
 
     // CLAMP: the tile may reach past the last key (rows are clamped to it).
-    template <bool CLAMP>
+    template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
-        const char* kb = p.k.base + static_cast<size_t>(tile * BN) * p.k.stride;
+        const char* kb = p.k.template tile_base<MAPPED>(tile);
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -314,10 +369,20 @@ struct Bf16QK {
             int row = idx / (D / 8);
             const int ch = idx % (D / 8);
             if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-            r.raw[i] = ld16(kb, row * p.k.stride + 16 * ch);
+            r.raw[i] = ld16(kb, p.k.template row_off<MAPPED>(tile, row) + 16 * ch);
             r.c0[i] = ld16f(tb, (row * D + 8 * ch) * 4);
             r.c1[i] = ld16f(tb, (row * D + 8 * ch + 4) * 4);
         }
+    }
+
+    // K' = RoPE(K) rounded once to fp16 (rot_pack_h2).
+    __device__ static __forceinline__ uint4 rotate8_k(const uint4& raw, const float4& c0, const float4& c1) {
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = rot_pack_h2(bf_lo(w[j]), bf_hi(w[j]), cs[2 * j], cs[2 * j + 1]);
+        return make_uint4(o[0], o[1], o[2], o[3]);
     }
 
     __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
@@ -327,7 +392,7 @@ struct Bf16QK {
             if (!has(i)) continue;
             const int idx = static_cast<int>(threadIdx.x % NT) + NT * i;
             const int row = idx / (D / 8), ch = idx % (D / 8);
-            *reinterpret_cast<uint4*>(kl + row * kStride + 8 * ch) = rotate8(r.raw[i], r.c0[i], r.c1[i], 1.0f);
+            *reinterpret_cast<uint4*>(kl + row * kStride + 8 * ch) = rotate8_k(r.raw[i], r.c0[i], r.c1[i]);
         }
     }
 
@@ -408,9 +473,10 @@ struct I16QK {
         m = make_uint2(mb[0], mb[1]);
     }
 
+    template <bool MAPPED>
     __device__ static __forceinline__ KPtr kptr(const RunArgs& a, const Ctx& c) {
-        return {kv_rows(a, c, a.k, D, 2), reinterpret_cast<const char*>(a.rope_q14 + static_cast<size_t>(c.off) * D),
-                c.S};
+        return {kv_rows<MAPPED>(a, c, a.k, D, 2),
+                reinterpret_cast<const char*>(a.rope_q14 + static_cast<size_t>(c.koff) * D), c.NK};
     }
 
     __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
@@ -440,9 +506,9 @@ struct I16QK {
 
     __device__ static __forceinline__ bool has(int i) { return kChunks % NT == 0 || static_cast<int>(threadIdx.x % NT) + NT * i < kChunks; }
 
-    template <bool CLAMP>
+    template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
-        const char* kb = p.k.base + static_cast<size_t>(tile * BN) * p.k.stride;
+        const char* kb = p.k.template tile_base<MAPPED>(tile);
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -450,7 +516,7 @@ struct I16QK {
             int row = idx / (D / 8);
             const int ch = idx % (D / 8);
             if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-            r.raw[i] = ld16(kb, row * p.k.stride + 16 * ch);
+            r.raw[i] = ld16(kb, p.k.template row_off<MAPPED>(tile, row) + 16 * ch);
             r.cs[i] = ld16(tb, (row * D + 8 * ch) * 2);
         }
     }
@@ -521,17 +587,18 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
         uint2 raw[kGran];
         float4 cs[kGran];
     };
-    template <bool CLAMP>
+    template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
         const int tid = threadIdx.x % NT;
         int row = tid >> 3;
         const int e0 = (tid & 7) * (D / 8);
         if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-        const char* kb = p.k.base + static_cast<size_t>(tile * BN) * p.k.stride;
+        const char* kb = p.k.template tile_base<MAPPED>(tile);
+        const uint32_t ro = p.k.template row_off<MAPPED>(tile, row);
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
 #pragma unroll
         for (int i = 0; i < kGran; ++i) {
-            r.raw[i] = *reinterpret_cast<const uint2*>(kb + row * p.k.stride + 2 * (e0 + 4 * i));
+            r.raw[i] = *reinterpret_cast<const uint2*>(kb + ro + 2 * (e0 + 4 * i));
             r.cs[i] = ld16f(tb, (row * D + e0 + 4 * i) * 4);
         }
     }
@@ -546,11 +613,7 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
             const float cs[4] = {r.cs[i].x, r.cs[i].y, r.cs[i].z, r.cs[i].w};
             uint32_t o[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float x = bf_lo(w[j]), y = bf_hi(w[j]);
-                const float c = cs[2 * j], sn = cs[2 * j + 1];
-                o[j] = pack_h2(fmaf(x, c, -y * sn), fmaf(x, sn, y * c));
-            }
+            for (int j = 0; j < 2; ++j) o[j] = rot_pack_h2(bf_lo(w[j]), bf_hi(w[j]), cs[2 * j], cs[2 * j + 1]);
             *reinterpret_cast<uint2*>(kl + 4 * i) = make_uint2(o[0], o[1]);
         }
     }
@@ -565,16 +628,17 @@ struct VStage8 : VStage<D, NT> {
     struct Regs {
         uint32_t w[2][kWords];
     };
-    template <bool CLAMP>
+    template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load(const Rows& p, int S, int tile, Regs& r) {
         const int tid = threadIdx.x % NT;
         const int kp = tid & 31, dg = tid >> 5;
-        const char* vb = p.base + static_cast<size_t>(tile * BN) * p.stride;
+        const char* vb = p.tile_base<MAPPED>(tile);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             int row = 2 * kp + kk;
             if (CLAMP) row = min(row, S - 1 - tile * BN);
-            const uint32_t* src = reinterpret_cast<const uint32_t*>(vb + row * p.stride + 2 * kDims * dg);
+            const uint32_t* src =
+                reinterpret_cast<const uint32_t*>(vb + p.row_off<MAPPED>(tile, row) + 2 * kDims * dg);
 #pragma unroll
             for (int i = 0; i < kWords; ++i) r.w[kk][i] = src[i];
         }
@@ -608,7 +672,8 @@ struct VStage8 : VStage<D, NT> {
 // so the matrix cores have independent work queued while the vector unit
 // runs the softmax and the staging.  Tiles every query of the workgroup sees
 // in full run a branch-free copy of the step (no masks, no clamps).
-template <int D, template <int, int> class QKT, template <int, int> class VST, int NW>
+// MAPPED: cached prefill, keys read through the index map (see Ctx).
+template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, bool MAPPED>
 struct FusedAttn {
     static constexpr int NT = 64 * NW;
     static constexpr int BMW = 32 * NW;
@@ -618,7 +683,7 @@ struct FusedAttn {
 
     char* lds;
     Ctx c;
-    int lq, lh, qw0, n_tiles;
+    int lq, lh, qw0, kq0, n_tiles;  // kq0: the wave's first query in key space
     typename P::KPtr kp;
     Rows vp;
     typename P::KRegs kr;
@@ -635,7 +700,7 @@ struct FusedAttn {
     __device__ __forceinline__ int nact(int t) const {
         if (qw0 >= c.S) return 0;
         const int kt0 = t * BN;
-        return kt0 + 32 <= qw0 + 31 ? 2 : (kt0 <= qw0 + 31 ? 1 : 0);
+        return kt0 + 32 <= kq0 + 31 ? 2 : (kt0 <= kq0 + 31 ? 1 : 0);
     }
 
     // Two sequential guards (not if / else-if), so the compiler cannot merge
@@ -654,10 +719,10 @@ struct FusedAttn {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const int k0 = t * BN + 32 * kb;
-                if (kb < na && k0 + 31 > qw0) {
+                if (kb < na && k0 + 31 > kq0) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
-                        if (k0 + acc_row(v, lh) > qw0 + lq) s[16 * kb + v] = kNegInf;
+                        if (k0 + acc_row(v, lh) > kq0 + lq) s[16 * kb + v] = kNegInf;
                 }
             }
         }
@@ -713,8 +778,8 @@ struct FusedAttn {
     __device__ __forceinline__ void step(int t, float* s, float* sn) {
         const bool ld_k = STEADY || t + 2 < n_tiles;
         const bool ld_v = STEADY || t + 1 < n_tiles;
-        if (ld_k) P::template load_k<!STEADY>(kp, t + 2, kr);
-        if (ld_v) V::template load<!STEADY>(vp, c.S, t + 1, vr);
+        if (ld_k) P::template load_k<!STEADY, MAPPED>(kp, t + 2, kr);
+        if (ld_v) V::template load<!STEADY, MAPPED>(vp, c.NK, t + 1, vr);
         const int na = STEADY ? 2 : nact(t);
         uint32_t pk[16];
         if (na > 0) softmax<STEADY>(t, na, s, pk);
@@ -731,18 +796,19 @@ struct FusedAttn {
         lq = lane & 31;
         lh = lane >> 5;
         qw0 = c.q0 + 32 * w;
-        n_tiles = (min(c.q0 + BMW, c.S) + BN - 1) / BN;
-        const int n_full = min(c.q0 / BN, n_tiles);  // tiles every query of the workgroup sees whole
-        kp = P::kptr(a, c);
-        vp = kv_rows(a, c, a.v, D, 2);
+        kq0 = c.kshift + qw0;
+        n_tiles = (c.kshift + min(c.q0 + BMW, c.S) + BN - 1) / BN;
+        const int n_full = min((c.kshift + c.q0) / BN, n_tiles);  // tiles every query of the workgroup sees whole
+        kp = P::template kptr<MAPPED>(a, c);
+        vp = kv_rows<MAPPED>(a, c, a.v, D, 2);
 
-        P::template load_k<true>(kp, 0, kr);
-        V::template load<true>(vp, c.S, 0, vr);
+        P::template load_k<true, MAPPED>(kp, 0, kr);
+        V::template load<true, MAPPED>(vp, c.NK, 0, vr);
         P::load_q(a, c, qw0 + lq, logit_scale, q);
         P::commit_k(kr, kbuf(0));
         V::commit(vr, vbuf(0));
         if (n_tiles > 1) {
-            P::template load_k<true>(kp, 1, kr);
+            P::template load_k<true, MAPPED>(kp, 1, kr);
             P::commit_k(kr, kbuf(1));
         }
 #pragma unroll
@@ -755,8 +821,11 @@ struct FusedAttn {
         qk_tile<false>(0, sa);
         __syncthreads();  // every wave has read K'(0) before step 0 overwrites that buffer
 
+        // A steady pair loads K(t+2), K(t+3) and V(t+1), V(t+2) unclamped and runs
+        // the softmax of tiles t, t+1 unmasked: every one of those tiles must lie
+        // below n_full (tile n_full itself may reach past the last key).
         int t = 0;
-        for (; t + 2 < n_full; t += 2) {
+        for (; t + 3 < n_full; t += 2) {
             step<true>(t, sa, sb);
             step<true>(t + 1, sb, sa);
         }
@@ -782,13 +851,13 @@ struct FusedAttn {
     }
 };
 
-template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, int MINB>
+template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, int MINB, bool MAPPED>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, float logit_scale) {
-    using K = FusedAttn<D, QKT, VST, NW>;
+    using K = FusedAttn<D, QKT, VST, NW, MAPPED>;
     __shared__ __attribute__((aligned(16))) char lds[K::kLds];
     K k;
     k.lds = lds;
-    if (!make_ctx<K::BMW>(a, k.c)) {
+    if (!make_ctx<K::BMW, MAPPED>(a, k.c)) {
         zero_rows<D, K::BMW, K::NT>(a, k.c);
         return;
     }
@@ -797,24 +866,25 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, floa
 
 // ------------------------------------------------ fp32 kernel (fp32 matrix cores)
 
-template <int D>
+template <int D, bool MAPPED>
 __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(RunArgs a, float logit_scale) {
     constexpr int kStride = D + 4;
     __shared__ __attribute__((aligned(16))) float ks_[BN * kStride];
     __shared__ __attribute__((aligned(16))) float vs_[BN * kStride];
 
     Ctx c;
-    if (!make_ctx<BM>(a, c)) {
+    if (!make_ctx<BM, MAPPED>(a, c)) {
         zero_rows<D, BM, kThreads>(a, c);
         return;
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lq = lane & 31, lh = lane >> 5;
     const int qw0 = c.q0 + 32 * w;
-    const int n_tiles = (min(c.q0 + BM, c.S) + BN - 1) / BN;
+    const int kq0 = c.kshift + qw0;
+    const int n_tiles = (c.kshift + min(c.q0 + BM, c.S) + BN - 1) / BN;
     const float* qg = static_cast<const float*>(a.q);
-    const float* kg = static_cast<const float*>(a.k);
-    const float* vg = static_cast<const float*>(a.v);
+    const Rows kr_ = kv_rows<MAPPED>(a, c, a.k, D, 4);
+    const Rows vr_ = kv_rows<MAPPED>(a, c, a.v, D, 4);
 
     // Q' of query qw0+lq: lane half lh keeps component lh of every pair (d = 2ks + lh).
     float qv[D / 2];
@@ -843,10 +913,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(RunArgs a, float
             const int row = idx / (D / 4), ch = idx % (D / 4);
             const int key = t * BN + row;
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx, tc = kx;
-            if (key < c.S) {
-                kx = *reinterpret_cast<const float4*>(kg + kv_index(a, c, key, D) + 4 * ch);
-                vx = *reinterpret_cast<const float4*>(vg + kv_index(a, c, key, D) + 4 * ch);
-                tc = *reinterpret_cast<const float4*>(a.rope_f32 + static_cast<size_t>(c.off + key) * D + 4 * ch);
+            if (key < c.NK) {
+                kx = ld16f(kr_.tile_base<MAPPED>(t), kr_.row_off<MAPPED>(t, row) + 16 * ch);
+                vx = ld16f(vr_.tile_base<MAPPED>(t), vr_.row_off<MAPPED>(t, row) + 16 * ch);
+                tc = *reinterpret_cast<const float4*>(a.rope_f32 + static_cast<size_t>(c.koff + key) * D + 4 * ch);
             }
             const float4 kr = make_float4(fmaf(kx.x, tc.x, -kx.y * tc.y), fmaf(kx.x, tc.y, kx.y * tc.x),
                                           fmaf(kx.z, tc.z, -kx.w * tc.w), fmaf(kx.z, tc.w, kx.w * tc.z));
@@ -855,7 +925,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(RunArgs a, float
         }
         __syncthreads();
         const int kt0 = t * BN;
-        int nact = kt0 + 32 <= qw0 + 31 ? 2 : (kt0 <= qw0 + 31 ? 1 : 0);
+        int nact = kt0 + 32 <= kq0 + 31 ? 2 : (kt0 <= kq0 + 31 ? 1 : 0);
         if (qw0 >= c.S) nact = 0;
         if (nact == 0) continue;
         float s[2][16];
@@ -868,7 +938,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(RunArgs a, float
             for (int k = 0; k < D / 2; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(row[2 * k], qv[k], acc, 0, 0, 0);
             const int k0 = kt0 + 32 * kb;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) s[kb][v] = (k0 + acc_row(v, lh) > qw0 + lq) ? kNegInf : acc[v];
+            for (int v = 0; v < 16; ++v) s[kb][v] = (k0 + acc_row(v, lh) > kq0 + lq) ? kNegInf : acc[v];
         }
         float mx = kNegInf;
 #pragma unroll
@@ -917,6 +987,38 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(RunArgs a, float
     }
 }
 
+// ------------------------------------------------ KV cache update
+
+// New token i of sequence b (logical position off[b] + i) is copied to slot
+// kv_map[b][off[b] + i] of the caches; nothing else is touched.  One thread
+// moves 16 bytes of K and 16 bytes of V.  A sequence whose chunk leaves the
+// map row, or a slot outside [0, n_slots), is skipped and sets the status word.
+__global__ __launch_bounds__(kThreads) void kv_cache_update_kernel(RunArgs a, uint32_t row_bytes, char* dk,
+                                                                   char* dv) {
+    const uint32_t chunks = row_bytes / 16;
+    const size_t g = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const size_t tok = g / chunks;
+    if (tok >= static_cast<size_t>(a.batch) * a.seq_len) return;
+    const uint32_t ch = static_cast<uint32_t>(g % chunks);
+    const int b = static_cast<int>(tok / a.seq_len), i = static_cast<int>(tok % a.seq_len);
+    const int off = a.pos_offsets ? a.pos_offsets[b] : 0;
+    if (off < 0 || static_cast<long long>(off) + a.seq_len > a.map_stride) {
+        if (ch == 0) atomicOr(a.status, 1);
+        return;
+    }
+    const int slot = a.kv_map[static_cast<size_t>(b) * a.map_stride + off + i];
+    if (static_cast<unsigned>(slot) >= static_cast<unsigned>(a.n_slots)) {
+        if (ch == 0) atomicOr(a.status, 1);
+        return;
+    }
+    const size_t src = tok * row_bytes + 16u * ch;
+    const size_t dst = static_cast<size_t>(slot) * row_bytes + 16u * ch;
+    const uint4 kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k) + src);
+    const uint4 vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) + src);
+    *reinterpret_cast<uint4*>(dk + dst) = kx;
+    *reinterpret_cast<uint4*>(dv + dst) = vx;
+}
+
 // ------------------------------------------------ int16 test kernels
 
 template <int D>
@@ -949,7 +1051,7 @@ __global__ __launch_bounds__(kThreads) void debug_scores_i32_kernel(RunArgs a, i
     using P = I16QK<D, kThreads>;
     __shared__ __attribute__((aligned(16))) char lds[P::kBytes];
     Ctx c;
-    if (!make_ctx<BM>(a, c)) {
+    if (!make_ctx<BM, false>(a, c)) {
         if (threadIdx.x == 0) atomicOr(a.status, 1);
         return;
     }
@@ -959,10 +1061,10 @@ __global__ __launch_bounds__(kThreads) void debug_scores_i32_kernel(RunArgs a, i
     typename P::Q q;
     P::load_q(a, c, qw0 + lq, 1.0f, q);
     const int n_tiles = (c.S + BN - 1) / BN;
-    const typename P::KPtr kp = P::kptr(a, c);
+    const typename P::KPtr kp = P::template kptr<false>(a, c);
     for (int t = 0; t < n_tiles; ++t) {
         typename P::KRegs kr;
-        P::template load_k<true>(kp, t, kr);
+        P::template load_k<true, false>(kp, t, kr);
         __syncthreads();
         P::commit_k(kr, lds);
         __syncthreads();
@@ -992,27 +1094,44 @@ dim3 grid_for(const RunArgs& a, int bm) {
 
 // 256-row eight-wave workgroups when they still give every CU work; otherwise
 // (short sequences, few heads) 128-row four-wave workgroups for parallelism.
-template <int D>
-hipError_t launch_bf16_d(const RunArgs& a, hipStream_t s) {
+// A non-null index map selects the cached-prefill instantiation.
+template <int D, bool M>
+void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
     const long long wgs256 = static_cast<long long>((a.seq_len + 255) / 256) * a.batch * a.n_heads;
     if (wgs256 >= 256) {
-        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1>), grid_for(a, 256), dim3(512), 0, s, a,
-                           a.score_scale * kLog2e);
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M>), grid_for(a, 256), dim3(512), 0, s,
+                           a, a.score_scale * kLog2e);
     } else {
-        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16QK, VStage, 4, 2>), grid_for(a, 128), dim3(256), 0, s, a,
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16QK, VStage, 4, 2, M>), grid_for(a, 128), dim3(256), 0, s, a,
                            a.score_scale * kLog2e);
     }
+}
+template <int D>
+hipError_t launch_bf16_d(const RunArgs& a, hipStream_t s) {
+    if (a.kv_map)
+        launch_bf16_dm<D, true>(a, s);
+    else
+        launch_bf16_dm<D, false>(a, s);
     return hipGetLastError();
 }
 template <int D>
 hipError_t launch_i16_d(const RunArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, I16QK, VStage, 4, 1>), grid_for(a, 128), dim3(256), 0, s, a,
-                       a.score_scale * kLog2e);
+    if (a.kv_map)
+        hipLaunchKernelGGL((attn_fwd_kernel<D, I16QK, VStage, 4, 1, true>), grid_for(a, 128), dim3(256), 0, s, a,
+                           a.score_scale * kLog2e);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<D, I16QK, VStage, 4, 1, false>), grid_for(a, 128), dim3(256), 0, s, a,
+                           a.score_scale * kLog2e);
     return hipGetLastError();
 }
 template <int D>
 hipError_t launch_f32_d(const RunArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), grid_for(a, BM), dim3(kThreads), 0, s, a, a.score_scale * kLog2e);
+    if (a.kv_map)
+        hipLaunchKernelGGL((attn_fwd_f32_kernel<D, true>), grid_for(a, BM), dim3(kThreads), 0, s, a,
+                           a.score_scale * kLog2e);
+    else
+        hipLaunchKernelGGL((attn_fwd_f32_kernel<D, false>), grid_for(a, BM), dim3(kThreads), 0, s, a,
+                           a.score_scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -1029,6 +1148,17 @@ hipError_t launch_f32_d(const RunArgs& a, hipStream_t s) {
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_bf16_d, head_dim, a, s) }
 hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_i16_d, head_dim, a, s) }
 hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_f32_d, head_dim, a, s) }
+
+hipError_t launch_kv_cache_update(int head_dim, int el, const RunArgs& a, void* dst_k, void* dst_v, hipStream_t s) {
+    const uint32_t row_bytes = static_cast<uint32_t>(a.n_kv_heads) * head_dim * el;
+    const size_t chunks = static_cast<size_t>(a.batch) * a.seq_len * (row_bytes / 16);
+    const size_t blocks = (chunks + kThreads - 1) / kThreads;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffu) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kv_cache_update_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a,
+                       row_bytes, static_cast<char*>(dst_k), static_cast<char*>(dst_v));
+    return hipGetLastError();
+}
 
 namespace {
 template <int D>

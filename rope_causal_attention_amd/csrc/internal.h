@@ -22,11 +22,22 @@ struct RunArgs {
     int n_kv_heads;
     int max_seq;
     float score_scale;           // resolved (never 0 here)
+    // Cached prefill only (kv_map non-null): k and v are caches [n_slots][n_kv_heads][D],
+    // kv_map[b * map_stride + j] is the slot of logical position j of sequence b, and
+    // pos_offsets[b] is the number of positions the cache held before this chunk.
+    const int32_t* kv_map;
+    int map_stride;
+    int n_slots;
 };
 
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t stream);
 hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t stream);
+
+// Copies the new tokens' K/V ([batch][seq_len][n_kv_heads][D], `el` bytes per
+// element) into their cache slots; a.k/a.v are the new K/V, dst_k/dst_v the caches.
+hipError_t launch_kv_cache_update(int head_dim, int el, const RunArgs& a, void* dst_k, void* dst_v,
+                                  hipStream_t stream);
 
 // Int16 test exports; RunArgs.q is the tensor to rotate (x) for the rope one,
 // q/k for the scores one; `dst` receives int16 x_rot or int32 scores.

@@ -91,6 +91,41 @@ def test_calls_on_null_handle():
     assert lib.prefill_attn_destroy(None) == pa.PA_OK
     assert lib.prefill_attn_debug_rope_i16(None, 1, 1, 16, 1, None, 16, None) == pa.PA_EINVAL
     assert lib.prefill_attn_debug_scores_i32(None, 1, 1, 16, 16, None, 16, None) == pa.PA_EINVAL
+    assert lib.prefill_attn_kv_cache_update(None, pa.PA_IN_BF16, 1, 4, 16, 16, None, 16, 4, 16, 16, 8,
+                                            None) == pa.PA_EINVAL
+    assert lib.prefill_attn_run_cached(None, pa.PA_IN_BF16, 1, 4, 16, 16, 16, 8, 16, 4, None, 16, 0.0,
+                                       None) == pa.PA_EINVAL
+
+
+@pytest.mark.parametrize("n_slots,start,count", [(128, 120, 12), (8, 0, 8), (5, 4, 23), (1, 0, 3), (16, 3, 0)])
+def test_ring_map_matches_oracle(n_slots, start, count):
+    got = pa.prefill_attn_ring_map(n_slots, start, count)
+    assert got.dtype == np.int32
+    assert got.astype(np.int64).tolist() == oracle.ring_index_map(n_slots, start, count).tolist()
+
+
+@pytest.mark.parametrize("table,block,count", [([3, 0, 2], 4, 10), ([7], 16, 16), ([5, 1, 9, 2], 1, 4),
+                                               ([2, 0], 64, 100)])
+def test_paged_map_matches_oracle(table, block, count):
+    got = pa.prefill_attn_paged_map(table, block, count)
+    assert got.astype(np.int64).tolist() == oracle.paged_index_map(table, block, count).tolist()
+
+
+def test_map_builders_reject_bad_arguments():
+    lib = pa.load_library()
+    buf = np.zeros(16, dtype=np.int32)
+    bt = np.array([1, 2], dtype=np.int32)
+    assert lib.prefill_attn_ring_map(0, 0, 4, buf.ctypes.data) == pa.PA_EINVAL        # no slots
+    assert lib.prefill_attn_ring_map(8, 8, 4, buf.ctypes.data) == pa.PA_EINVAL        # start outside the ring
+    assert lib.prefill_attn_ring_map(8, 0, -1, buf.ctypes.data) == pa.PA_EINVAL
+    assert lib.prefill_attn_ring_map(8, 0, 4, None) == pa.PA_EINVAL
+    assert lib.prefill_attn_paged_map(bt.ctypes.data, 2, 4, 9, buf.ctypes.data) == pa.PA_EINVAL  # 3 blocks needed
+    assert lib.prefill_attn_paged_map(bt.ctypes.data, 2, 0, 4, buf.ctypes.data) == pa.PA_EINVAL  # block size 0
+    neg = np.array([-1], dtype=np.int32)
+    assert lib.prefill_attn_paged_map(neg.ctypes.data, 1, 4, 4, buf.ctypes.data) == pa.PA_EINVAL
+    big = np.array([1 << 30], dtype=np.int32)
+    assert lib.prefill_attn_paged_map(big.ctypes.data, 1, 4, 4, buf.ctypes.data) == pa.PA_EINVAL  # slot >= 2^31
+    assert lib.prefill_attn_paged_map(None, 0, 4, 0, None) == pa.PA_OK
 
 
 def test_strerror_covers_every_code():

@@ -1,0 +1,340 @@
+"""GPU parity of the KV-cache path: kv_cache_update and cached (chunked)
+prefill through the C-ABI, against the fp64 oracle and against the plain
+prefill path.
+
+* the cache update is byte work: compared bit for bit;
+* a cached run with the identity map and no prefix is the plain prefill and
+  must match it bit for bit (same kernels, only the key addressing differs);
+* chunked prefill through ring and paged maps, with ragged prefixes and
+  garbage in unused slots, is compared with the oracle at the tolerances of
+  the plain path (fp32 max-abs 1e-5; bf16 and int16 output max-abs 1e-2,
+  mean-abs 1e-3), and with the plain prefill of the whole sequence.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rope_causal_attention_amd as pa
+import synth
+from gpu_common import announce, assert_close, errors, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "i16": torch.int16}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _seed(name):
+    return sum(map(ord, name))
+
+
+def _score_scale(dt, D):
+    return 2.0 ** -22 / np.sqrt(D) if dt == "i16" else 0.0
+
+
+def _garbage(shape, dt, seed):
+    g = torch.Generator().manual_seed(seed)
+    if dt == "i16":
+        return torch.randint(-2048, 2048, shape, generator=g, dtype=torch.int16)
+    return (torch.randn(shape, generator=g) * 4.0).to(TORCH_DT[dt])
+
+
+def _maps(layout, B, width, n_slots, seed, block=16):
+    """Distinct slots for every (b, logical position < width)."""
+    rng = np.random.default_rng(seed)
+    if layout == "identity":
+        assert B == 1
+        return np.arange(width, dtype=np.int32)[None, :]
+    if layout == "ring":
+        per = n_slots // B
+        return np.stack([oracle.ring_index_map(per, int(rng.integers(per)), width) + b * per
+                         for b in range(B)]).astype(np.int32)
+    assert layout == "paged"
+    nb = n_slots // block
+    blocks = rng.permutation(nb)
+    need = (width + block - 1) // block
+    return np.stack([oracle.paged_index_map(blocks[b * need:(b + 1) * need], block, width)
+                     for b in range(B)]).astype(np.int32)
+
+
+class Case:
+    """Full logical sequences, a cache holding them, and the chunk's queries."""
+
+    def __init__(self, name, B, Hq, Hkv, D, dt, theta, prefix, S, layout, n_slots):
+        self.name, self.dt, self.theta, self.prefix, self.S = name, dt, theta, list(prefix), S
+        self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
+        self.width = max(prefix) + S
+        w = synth.Workload(name, B, Hq, Hkv, self.width, D, dt, theta, _seed(name))
+        self.q_all, self.k_all, self.v_all = synth.make_inputs(w)
+        self.q = torch.stack([self.q_all[b, p:p + S] for b, p in enumerate(prefix)]).contiguous()
+        self.n_slots = n_slots
+        self.map = _maps(layout, B, self.width, n_slots, _seed(name) + 1)
+        self.kc = _garbage((n_slots, Hkv, D), dt, _seed(name) + 2)
+        self.vc = _garbage((n_slots, Hkv, D), "bf16" if dt == "i16" else dt, _seed(name) + 3)
+        for b, p in enumerate(prefix):
+            slots = torch.from_numpy(self.map[b, :p + S].astype(np.int64))
+            self.kc[slots] = self.k_all[b, :p + S]
+            self.vc[slots] = self.v_all[b, :p + S]
+        self.scale = _score_scale(dt, D)
+
+    def oracle(self):
+        f = synth.to_f64
+        if self.dt == "i16":
+            return oracle.attention_i16_cached(f(self.q), f(self.kc), f(self.vc), self.map, self.prefix,
+                                               rope_theta=self.theta, score_scale=self.scale)
+        return oracle.attention_cached(f(self.q), f(self.kc), f(self.vc), self.map, self.prefix,
+                                       rope_theta=self.theta, scale=self.scale or None)
+
+    def run(self, attn):
+        dev = lambda t: t.cuda()  # noqa: E731
+        off = torch.tensor(self.prefix, dtype=torch.int32, device="cuda")
+        o = attn.run_cached(dev(self.q), dev(self.kc), dev(self.vc), dev(torch.from_numpy(self.map)),
+                            pos_offsets=off, score_scale=self.scale)
+        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
+        return o.cpu()
+
+
+def _handle(c, max_seq=None):
+    return pa.PrefillAttention(c.Hq, c.Hkv, c.D, max_seq or c.width, c.theta)
+
+
+# ------------------------------------------------------------ cache update
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "i16"])
+def test_cache_update_is_bit_exact(dt):
+    name = f"upd_{dt}"
+    announce(name)
+    B, S, Hkv, D, n_slots = 3, 37, 2, 128 if dt != "f32" else 64, 512
+    prefix = [0, 5, 64]
+    width = max(prefix) + S
+    kv_map = _maps("paged", B, width, n_slots, _seed(name))
+    kc = _garbage((n_slots, Hkv, D), dt, 1)
+    vdt = "bf16" if dt == "i16" else dt
+    vc = _garbage((n_slots, Hkv, D), vdt, 2)
+    kn = _garbage((B, S, Hkv, D), dt, 3)
+    vn = _garbage((B, S, Hkv, D), vdt, 4)
+    attn = pa.PrefillAttention(4, Hkv, D, width, 1e4)
+    try:
+        kcd, vcd = kc.cuda(), vc.cuda()
+        off = torch.tensor(prefix, dtype=torch.int32, device="cuda")
+        attn.kv_cache_update(kn.cuda(), vn.cuda(), kcd, vcd, torch.from_numpy(kv_map).cuda(), off)
+        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
+        bits = torch.int32 if dt == "f32" else torch.int16
+        want_k, want_v = oracle.kv_cache_update(kc.view(bits).numpy(), vc.view(bits).numpy(), kn.view(bits).numpy(),
+                                                vn.view(bits).numpy(), kv_map, prefix)
+        assert np.array_equal(kcd.cpu().view(bits).numpy(), want_k)
+        assert np.array_equal(vcd.cpu().view(bits).numpy(), want_v)
+    finally:
+        attn.close()
+
+
+# ------------------------------------------------------------ cached == plain
+
+PLAIN_CASES = [
+    # name, B, Hq, Hkv, S, D, dtype, theta
+    ("same_bf16_4wave", 1, 4, 2, 300, 128, "bf16", 1e4),
+    ("same_bf16_8wave", 1, 64, 8, 1030, 96, "bf16", 1e4),
+    ("same_f32", 1, 2, 1, 200, 64, "f32", 1e4),
+    ("same_i16", 1, 4, 4, 300, 128, "i16", 1e4),
+]
+
+
+@pytest.mark.parametrize("case", PLAIN_CASES, ids=[c[0] for c in PLAIN_CASES])
+def test_identity_map_equals_plain_prefill_bitwise(case):
+    name, B, Hq, Hkv, S, D, dt, theta = case
+    announce(name)
+    w = synth.Workload(name, B, Hq, Hkv, S, D, dt, theta, _seed(name), score_scale=_score_scale(dt, D))
+    q, k, v = synth.make_inputs(w)
+    attn = pa.PrefillAttention(Hq, Hkv, D, S, theta)
+    try:
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        o_plain = attn(qd, kd, vd, score_scale=w.score_scale)
+        ident = torch.arange(S, dtype=torch.int32, device="cuda")[None, :]
+        o_cached = attn.run_cached(qd, kd[0], vd[0], ident, score_scale=w.score_scale)
+        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
+        assert torch.equal(o_plain, o_cached)
+    finally:
+        attn.close()
+
+
+# ------------------------------------------------------------ cached vs oracle
+
+SMALL_CASES = [
+    # name, B, Hq, Hkv, D, dtype, theta, prefix, S, layout, n_slots
+    ("c_bf16_d64_ring", 2, 4, 2, 64, "bf16", 1e4, [0, 77], 150, "ring", 1024),
+    ("c_bf16_d96_paged", 3, 4, 1, 96, "bf16", 1e4, [64, 300, 5], 129, "paged", 2048),
+    ("c_bf16_d128_paged", 2, 8, 2, 128, "bf16", 1e6, [256, 1], 200, "paged", 1024),
+    ("c_bf16_d128_decode_shape", 2, 4, 4, 128, "bf16", 1e4, [700, 1023], 1, "paged", 2048),
+    ("c_f32_d64_paged", 2, 2, 1, 64, "f32", 1e4, [33, 128], 70, "paged", 512),
+    ("c_f32_d128_ring", 1, 2, 2, 128, "f32", 1e4, [190], 66, "ring", 300),
+    ("c_i16_d128_paged", 2, 4, 2, 128, "i16", 1e4, [100, 0], 160, "paged", 1024),
+    ("c_i16_d64_ring", 1, 2, 1, 64, "i16", 1e4, [64], 64, "ring", 200),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_cached_prefill_matches_oracle(case):
+    c = Case(*case)
+    announce(c.name)
+    attn = _handle(c)
+    try:
+        got = c.run(attn)
+    finally:
+        attn.close()
+    mx, mean = assert_close(got.numpy(), c.oracle(), "f32" if c.dt == "f32" else "bf16")
+    announce(c.name, f"max {mx:.2e} mean {mean:.2e}")
+
+
+# ------------------------------------------------------------ chunked pipelines
+
+def _chunked(attn, q, k, v, chunks, kv_map, n_slots, dt, scale):
+    """kv_cache_update + run_cached per chunk on device tensors; returns O [B][T][Hq][D]."""
+    B, T, Hkv, D = k.shape
+    kc = torch.zeros((n_slots, Hkv, D), dtype=k.dtype, device="cuda")
+    vc = torch.zeros((n_slots, Hkv, D), dtype=v.dtype, device="cuda")
+    mapd = torch.from_numpy(kv_map).cuda()
+    outs, pos = [], 0
+    for n in chunks:
+        off = torch.full((B,), pos, dtype=torch.int32, device="cuda")
+        attn.kv_cache_update(k[:, pos:pos + n].contiguous(), v[:, pos:pos + n].contiguous(), kc, vc, mapd, off)
+        outs.append(attn.run_cached(q[:, pos:pos + n].contiguous(), kc, vc, mapd, pos_offsets=off, score_scale=scale))
+        pos += n
+    torch.cuda.synchronize()
+    assert attn.status() == pa.PA_OK
+    return torch.cat(outs, dim=1)
+
+
+@pytest.mark.parametrize("name,B,Hq,Hkv,D,chunks", [
+    ("chunk_8wave_d128", 4, 32, 8, 128, [512, 512, 512]),
+    ("chunk_8wave_odd_tiles", 4, 32, 8, 128, [320, 704]),  # prefix 320: an odd count of whole tiles
+    ("chunk_ragged_d64", 2, 8, 2, 64, [100, 333, 1, 250]),
+])
+def test_chunked_prefill_equals_plain_prefill(name, B, Hq, Hkv, D, chunks):
+    T = sum(chunks)
+    announce(name, chunks)
+    w = synth.Workload(name, B, Hq, Hkv, T, D, "bf16", 1e4, _seed(name))
+    q, k, v = synth.make_inputs(w)
+    n_slots = B * ((T + 63) // 64) * 64 + 64
+    kv_map = _maps("paged", B, T, n_slots, _seed(name), block=64)
+    attn = pa.PrefillAttention(Hq, Hkv, D, T, 1e4)
+    try:
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        o_chunk = _chunked(attn, qd, kd, vd, chunks, kv_map, n_slots, "bf16", 0.0).cpu()
+        o_plain = attn(qd, kd, vd).cpu()
+    finally:
+        attn.close()
+    # Chunk boundaries at multiples of 64 keep the same key tiles as the plain run.
+    if all(n % 64 == 0 for n in chunks):
+        assert torch.equal(o_chunk, o_plain)
+    else:
+        mx, _ = errors(o_chunk.numpy(), o_plain.numpy())
+        assert mx <= 2e-3, mx
+    rng = np.random.default_rng(3)
+    rows = sorted({(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(48)}
+                  | {(0, 0, 0), (B - 1, Hq - 1, T - 1)})
+    want = oracle.attention_rows(q.float().numpy(), k.float().numpy(), v.float().numpy(), rows, rope_theta=1e4)
+    got = np.stack([o_chunk[b, i, h].numpy() for b, h, i in rows])
+    mx, _ = errors(got, want)
+    assert mx <= 1e-2, mx
+
+
+def test_long_prompt_in_four_chunks():
+    """The 1 x 32 x 4096 x 96 long prompt, prefilled in chunks of 1024 through a
+    ring cache: equal to the one-shot prefill, and to the oracle on sampled rows."""
+    w = synth.WORKLOADS["mha_bf16_h32_s4096_d96"]
+    announce(w.name, "chunks of 1024")
+    q, k, v = synth.make_inputs(w)
+    kv_map = oracle.ring_index_map(4096, 1000, 4096).astype(np.int32)[None, :]
+    attn = pa.PrefillAttention(w.n_heads, w.n_kv_heads, w.head_dim, w.seq_len, w.rope_theta)
+    try:
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        o_chunk = _chunked(attn, qd, kd, vd, [1024] * 4, kv_map, 4096, "bf16", 0.0).cpu()
+        o_plain = attn(qd, kd, vd).cpu()
+    finally:
+        attn.close()
+    assert torch.equal(o_chunk, o_plain)
+    from gpu_common import oracle_rows, sample_rows
+    rows = sample_rows(w, 64, seed=11)
+    want = oracle_rows(w, q, k, v, rows)
+    got = np.stack([o_chunk[b, i, h].numpy() for b, h, i in rows])
+    mx, _ = errors(got, want)
+    assert mx <= 1e-2, mx
+
+
+# ------------------------------------------------------------ range errors
+
+def test_bad_slot_is_read_as_slot_zero_and_reported():
+    c = Case("bad_slot", 1, 2, 2, 64, "bf16", 1e4, [40], 30, "paged", 256)
+    announce(c.name)
+    attn = _handle(c)
+    try:
+        bad = c.map.copy()
+        bad[0, 7] = c.n_slots + 5
+        off = torch.tensor(c.prefix, dtype=torch.int32, device="cuda")
+        o = attn.run_cached(c.q.cuda(), c.kc.cuda(), c.vc.cuda(), torch.from_numpy(bad).cuda(), pos_offsets=off)
+        assert attn.status() == pa.PA_ERANGE
+        assert torch.all(torch.isfinite(o))
+        # the update skips the token whose slot is out of range
+        kc, vc = c.kc.cuda(), c.vc.cuda()
+        bad[0, 45] = -3
+        kn = _garbage((1, 30, 2, 64), "bf16", 9).cuda()
+        attn.kv_cache_update(kn, kn, kc, vc, torch.from_numpy(bad).cuda(), off)
+        assert attn.status() == pa.PA_ERANGE
+        slots = bad[0, 40:70]
+        for i, s in enumerate(slots):
+            if 0 <= s < c.n_slots:
+                assert torch.equal(kc[s].cpu(), kn[0, i].cpu())
+    finally:
+        attn.close()
+
+
+def test_chunk_past_the_map_row_zeroes_that_sequence():
+    c = Case("short_map", 2, 2, 1, 64, "bf16", 1e4, [10, 20], 40, "paged", 512)
+    announce(c.name)
+    attn = _handle(c, max_seq=256)
+    try:
+        off = torch.tensor([10, 30], dtype=torch.int32, device="cuda")  # 30 + 40 > map_stride 60
+        out = torch.full(c.q.shape, 7.0, dtype=torch.float32, device="cuda")
+        attn.run_cached(c.q.cuda(), c.kc.cuda(), c.vc.cuda(), torch.from_numpy(c.map).cuda(), pos_offsets=off,
+                        out=out)
+        assert attn.status() == pa.PA_ERANGE
+        o = out.cpu()
+        assert torch.all(o[1] == 0)
+        assert torch.all(torch.isfinite(o[0])) and not torch.all(o[0] == 7.0)
+    finally:
+        attn.close()
+
+
+def test_cache_calls_reject_bad_arguments():
+    attn = pa.PrefillAttention(2, 2, 64, 64, 1e4)
+    lib = pa.load_library()
+    try:
+        buf = torch.zeros(1 << 16, dtype=torch.float32, device="cuda")
+        p = buf.data_ptr()
+        h = attn.handle
+        s = torch.cuda.current_stream().cuda_stream
+        run = lambda *a: lib.prefill_attn_run_cached(h, *a)  # noqa: E731
+        upd = lambda *a: lib.prefill_attn_kv_cache_update(h, *a)  # noqa: E731
+        assert run(pa.PA_IN_BF16, 1, 8, p, p, p, 0, p, 8, None, p, 0.0, s) == pa.PA_EINVAL    # no slots
+        assert run(pa.PA_IN_BF16, 1, 8, p, p, p, 16, p, 4, None, p, 0.0, s) == pa.PA_EINVAL   # map row < chunk
+        assert run(pa.PA_IN_BF16, 1, 8, p, p, p, 16, None, 8, None, p, 0.0, s) == pa.PA_EINVAL  # no map
+        assert run(pa.PA_IN_BF16, 1, 8, p, p, p, 16, p + 2, 8, None, p, 0.0, s) == pa.PA_EINVAL  # misaligned map
+        assert run(pa.PA_IN_BF16, 1, 8, p, p + 8, p, 16, p, 8, None, p, 0.0, s) == pa.PA_EINVAL  # misaligned cache
+        assert run(pa.PA_IN_BF16, 1, 8, p, p, p, 1 << 24, p, 8, None, p, 0.0, s) == pa.PA_EINVAL  # cache > 4 GiB
+        assert run(9, 1, 8, p, p, p, 16, p, 8, None, p, 0.0, s) == pa.PA_EINVAL
+        assert upd(pa.PA_IN_BF16, 1, 8, p, p, None, p, 4, p, p, 16, s) == pa.PA_EINVAL
+        assert upd(pa.PA_IN_BF16, 1, 8, p, None, None, p, 8, p, p, 16, s) == pa.PA_EINVAL
+        assert upd(pa.PA_IN_BF16, 0, 8, None, None, None, None, 8, None, None, 16, s) == pa.PA_OK
+        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
+    finally:
+        attn.close()
