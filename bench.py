@@ -9,6 +9,18 @@ with per-head scales, RoPE theta 1e4, causal).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--cpu-budget SECONDS | --no-cpu-baseline] [--calib-copy]
+                    [--mode prefill|chunked|decode] [--chunk N]
+
+--mode chunked prefills the same prompt in chunks of N tokens through a KV
+cache (a ring of seq_len slots): each chunk's K/V is copied into the cache
+(prefill_attn_kv_cache_update), then its queries attend to every cached key
+(prefill_attn_run_cached).  A step is the whole prompt, all chunks.
+
+--mode decode times decode attention (prefill_attn_decode): 16 sequences each
+with one new token at position 4095 against a paged bf16 KV cache of 4096
+tokens, 32 query / 8 KV heads of dimension 128.  A step is one new token for
+every sequence; the roofline is HBM bandwidth (every cached K and V row read
+once).
 """
 
 import argparse
@@ -104,6 +116,64 @@ def cpu_baseline(w, budget_s):
     }
 
 
+DECODE = dict(batch=16, ctx=4096, n_heads=32, n_kv_heads=8, head_dim=128, rope_theta=1e4, block=64, seed=2024)
+
+
+def bench_decode(args, torch, pa):
+    """Decode attention over a paged bf16 cache; prints one JSON line."""
+    import numpy as np
+
+    c = DECODE
+    B, T, Hq, Hkv, D = c["batch"], c["ctx"], c["n_heads"], c["n_kv_heads"], c["head_dim"]
+    g = torch.Generator().manual_seed(c["seed"])
+    n_blocks = B * T // c["block"]
+    kc = torch.randn((n_blocks * c["block"], Hkv, D), generator=g).to(torch.bfloat16).cuda()
+    vc = torch.randn((n_blocks * c["block"], Hkv, D), generator=g).to(torch.bfloat16).cuda()
+    q = torch.randn((B, Hq, D), generator=g).to(torch.bfloat16).cuda()
+    perm = np.random.default_rng(c["seed"]).permutation(n_blocks)
+    per = T // c["block"]
+    rows = [pa.prefill_attn_paged_map(perm[b * per:(b + 1) * per], c["block"], T) for b in range(B)]
+    kv_map = torch.from_numpy(np.stack(rows)).cuda()
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+    attn = pa.PrefillAttention(Hq, Hkv, D, T, c["rope_theta"])
+    ws = torch.empty(pa.prefill_attn_decode_workspace_size(attn.handle, B, 64), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        attn.decode(q, kc, vc, kv_map, pos_offsets=pos, workspace=ws, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if attn.status() != pa.PA_OK:
+        raise RuntimeError("status word set during warm-up")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # K and V rows read once, q read, O written, the map row read.
+    algo = 2 * B * T * Hkv * D * 2 + B * Hq * D * 2 + B * Hq * D * 4 + B * T * 4
+    gbs = algo / (ms * 1e-3) / 1e9
+    log(f"decode: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s = {100 * gbs / 8000:.1f}% of 8 TB/s")
+    print(json.dumps({
+        "metric": "decode attention over a KV cache: new tokens/s (HBM GB/s)",
+        "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode_bf16_b{B}_h{Hq}kv{Hkv}_ctx{T}_d{D}", "batch": B, "context": T,
+                   "n_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "input_dtype": "bf16", "cache": "paged, 64"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": 8000.0, "unit": "GB/s", "frac": gbs / 8000.0,
+                     "traffic": None, "algorithmic_bytes": algo},
+        "cpu_baseline": None,
+    }), flush=True)
+    attn.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +184,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB elementwise copy (HBM counter calibration)")
+    ap.add_argument("--mode", choices=["prefill", "chunked", "decode"], default="prefill")
+    ap.add_argument("--chunk", type=int, default=1024, help="chunk length for --mode chunked")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -126,16 +198,36 @@ def main():
     import rope_causal_attention_amd as pa
     import synth
 
-    w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.mode == "decode":
+        return bench_decode(args, torch, pa)
+    w = synth.WORKLOADS[args.workload]
     q, k, v = synth.make_inputs(w)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     out = torch.empty((w.batch, w.seq_len, w.n_heads, w.head_dim), dtype=torch.float32, device="cuda")
     attn = pa.PrefillAttention(w.n_heads, w.n_kv_heads, w.head_dim, w.max_seq or w.seq_len, w.rope_theta)
     stream = torch.cuda.current_stream()
 
-    def step():
-        attn(qd, kd, vd, score_scale=w.score_scale, out=out, stream=stream)
+    if args.mode == "prefill":
+        def step():
+            attn(qd, kd, vd, score_scale=w.score_scale, out=out, stream=stream)
+    else:
+        # Ring cache of seq_len slots starting at slot 1000 (wraps), one map row per sequence.
+        S, B = w.seq_len, w.batch
+        kc = torch.empty((B * S, w.n_kv_heads, w.head_dim), dtype=kd.dtype, device="cuda")
+        vc = torch.empty((B * S, w.n_kv_heads, w.head_dim), dtype=vd.dtype, device="cuda")
+        ring = [pa.prefill_attn_ring_map(S, 1000 % S, S).astype("int64") + b * S for b in range(B)]
+        kv_map = torch.tensor(ring, dtype=torch.int32, device="cuda")
+        chunks = [(p, min(args.chunk, S - p)) for p in range(0, S, args.chunk)]
+        pieces = [(torch.full((B,), p, dtype=torch.int32, device="cuda"), qd[:, p:p + n].contiguous(),
+                   kd[:, p:p + n].contiguous(), vd[:, p:p + n].contiguous()) for p, n in chunks]
+        outs = [torch.empty(x[1].shape, dtype=torch.float32, device="cuda") for x in pieces]
+
+        def step():
+            for (off, qc, kn, vn), oc in zip(pieces, outs):
+                attn.kv_cache_update(kn, vn, kc, vc, kv_map, off, stream=stream)
+                attn.run_cached(qc, kc, vc, kv_map, pos_offsets=off, score_scale=w.score_scale, out=oc,
+                                stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -164,7 +256,7 @@ def main():
     if attn.status() != pa.PA_OK:
         raise RuntimeError("status word set during the timed steps")
     ms = e0.elapsed_time(e1) / args.steps
-    log(f"{w.name}: {ms * 1e3:.1f} us/step (host wall {t_host / args.steps * 1e6:.1f} us/step)")
+    log(f"{w.name} [{args.mode}]: {ms * 1e3:.1f} us/step (host wall {t_host / args.steps * 1e6:.1f} us/step)")
 
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -172,7 +264,7 @@ def main():
     log(f"{tflops:.1f} TFLOP/s = {100 * tflops / PEAK_TFLOPS:.1f}% of {PEAK_TFLOPS} ; {tokens_s:.4g} tokens/s")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.mode == "prefill":
         cpu = cpu_baseline(w, args.cpu_budget)
         log(f"cpu oracle: {cpu['value']:.4g} tokens/s on {cpu['cores']} BLAS threads ({cpu['sample']})")
 
@@ -190,7 +282,8 @@ def main():
         "dtype": "f16" if w.dtype == "bf16" else {"f32": "f32", "i16": "i8"}[w.dtype],
         "data": "synthetic",
         "config": {
-            "workload": w.name,
+            "workload": w.name if args.mode == "prefill" else f"{w.name}, chunked prefill in chunks of {args.chunk}",
+            "mode": args.mode,
             "batch": w.batch,
             "seq_len": w.seq_len,
             "n_heads": w.n_heads,
@@ -208,7 +301,7 @@ def main():
             "peak": PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": tflops / PEAK_TFLOPS,
-            "traffic": traffic_record(w),
+            "traffic": traffic_record(w) if args.mode == "prefill" else None,
             "algorithmic_bytes": algorithmic_bytes(w),
         },
         "cpu_baseline": cpu,

@@ -42,6 +42,7 @@
 #ifndef PREFILL_ATTN_H
 #define PREFILL_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -148,6 +149,40 @@ int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int batch, int 
                             const void* q, const void* k_cache, const void* v_cache, int n_slots,
                             const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
                             float* out, float score_scale, void* stream);
+
+/*
+ * Decode attention: one new token per sequence against the KV cache.
+ *
+ * Sources: the page titled "手写内核实现6倍prefill加速", §3.1 (RoPE from
+ * position-indexed tables) and §3.2 (keys read through the index map in
+ * logical order); the MNN-on-K3 blog (zhaode.wang/blog/2026/mnn-k3-riscv),
+ * §五 and §六: decode attention is a short matrix-vector product limited by
+ * memory bandwidth, computed as blocked online softmax.
+ *
+ * For sequence b, with P = pos_offsets[b] (NULL = all 0) the position of its
+ * new token, whose K/V must already be in the cache at logical position P:
+ *     out[b,h,:] = sum_{j <= P} softmax_j( RoPE_P(q[b,h]) . RoPE_j(Kc[map(b,j), kvh(h)]) * scale ) Vc[map(b,j), kvh(h)]
+ * i.e. prefill_attn_run_cached with seq_len = 1.  q is [batch][n_heads][head_dim],
+ * out [batch][n_heads][head_dim] float32, caches and kv_map as for the cache calls
+ * above.  in_dtype is PA_IN_F32 or PA_IN_BF16 (caches of the same type); all
+ * arithmetic is fp32.
+ *
+ * The keys of a sequence are split over n_split workgroups (0 = chosen by the
+ * library so that about a thousand workgroups run); with n_split > 1 the partial
+ * results go to `workspace` (device, 16-byte aligned, caller-owned, at least
+ * prefill_attn_decode_workspace_size(h, batch, n_split) bytes) and a second
+ * kernel merges them.  If the workspace is NULL or too small the call uses the
+ * largest split it can hold (n_split = 1 needs none).  Asynchronous, no
+ * allocation.  PA_EINVAL for bad shapes or pointers as for the cache calls; a
+ * sequence with P < 0, P + 1 > map_stride or P + 1 > max_seq gets out = 0 and
+ * sets the status word, as does a map entry outside [0, n_slots) (read as slot 0).
+ */
+size_t prefill_attn_decode_workspace_size(const prefill_attn* h, int batch, int n_split);
+int prefill_attn_decode(const prefill_attn* h, int in_dtype, int batch, const void* q,
+                        const void* k_cache, const void* v_cache, int n_slots,
+                        const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
+                        float* out, float score_scale, int n_split,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Host-only index-map builders (caller-owned host arrays; copy the result to the

@@ -25,6 +25,7 @@ __all__ = [
     "prefill_attn_strerror", "prefill_attn_rope_table_f32", "prefill_attn_rope_table_q14",
     "prefill_attn_debug_rope_i16", "prefill_attn_debug_scores_i32",
     "prefill_attn_kv_cache_update", "prefill_attn_run_cached", "prefill_attn_ring_map", "prefill_attn_paged_map",
+    "prefill_attn_decode", "prefill_attn_decode_workspace_size",
     "PrefillAttention", "EXPORTED_SYMBOLS",
 ]
 
@@ -50,6 +51,9 @@ _SIGNATURES = {
     "prefill_attn_run_cached": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _P]),
     "prefill_attn_ring_map": (_I, [_I, _I, _I, _P]),
     "prefill_attn_paged_map": (_I, [_P, _I, _I, _I, _P]),
+    "prefill_attn_decode_workspace_size": (ctypes.c_size_t, [_P, _I, _I]),
+    "prefill_attn_decode": (_I, [_P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _I, _P,
+                                 ctypes.c_size_t, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -222,6 +226,21 @@ def prefill_attn_paged_map(block_table, block_size, count):
     return out[:count]
 
 
+def prefill_attn_decode_workspace_size(handle, batch, n_split):
+    """Bytes of workspace a decode call with n_split > 1 needs (0 for n_split = 1)."""
+    return int(load_library().prefill_attn_decode_workspace_size(handle, batch, n_split))
+
+
+def prefill_attn_decode(handle, in_dtype, batch, q, k_cache, v_cache, n_slots, kv_map, map_stride, pos_offsets,
+                        out, score_scale=0.0, n_split=0, workspace=None, workspace_bytes=0, stream=None):
+    """Enqueue one decode-attention pass (see the header)."""
+    _check(load_library().prefill_attn_decode(handle, in_dtype, batch, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                              n_slots, _ptr(kv_map), map_stride, _ptr(pos_offsets), _ptr(out),
+                                              float(score_scale), n_split, _ptr(workspace), int(workspace_bytes),
+                                              _stream(stream)),
+           "prefill_attn_decode")
+
+
 # ------------------------------------------------------------- tensor helper
 
 _DTYPES = {torch.float32: PA_IN_F32, torch.bfloat16: PA_IN_BF16, torch.int16: PA_IN_I16}
@@ -332,4 +351,28 @@ class PrefillAttention:
             raise ValueError("out must be contiguous float32 [B][S][n_heads][head_dim]")
         prefill_attn_run_cached(self.handle, dt, B, S, q, k_cache, v_cache, n_slots, kv_map, stride, pos_offsets,
                                 out, score_scale, stream)
+        return out
+
+    def decode(self, q, k_cache, v_cache, kv_map, pos_offsets=None, score_scale=0.0, n_split=0, workspace=None,
+               out=None, stream=None):
+        """One new token per sequence: q [B][n_heads][head_dim] (float32 or bfloat16) at
+        position pos_offsets[b] against cached keys 0 .. pos_offsets[b].  Returns O
+        float32 [B][n_heads][head_dim].  workspace: a device tensor (any dtype) or None."""
+        if q.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("decode takes float32 or bfloat16 q")
+        dt = _DTYPES[q.dtype]
+        B = q.shape[0]
+        if tuple(q.shape) != (B, self.n_heads, self.head_dim) or not q.is_cuda or not q.is_contiguous():
+            raise ValueError("q must be a contiguous device tensor [B][n_heads][head_dim]")
+        n_slots, stride = self._check_cache(k_cache, v_cache, kv_map, dt, B)
+        if pos_offsets is not None and (pos_offsets.dtype != torch.int32 or pos_offsets.numel() != B
+                                        or not pos_offsets.is_cuda):
+            raise ValueError("pos_offsets must be a device int32 tensor with one entry per batch element")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        elif out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+            raise ValueError("out must be contiguous float32 [B][n_heads][head_dim]")
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        prefill_attn_decode(self.handle, dt, B, q, k_cache, v_cache, n_slots, kv_map, stride, pos_offsets, out,
+                            score_scale, n_split, workspace, ws_bytes, stream)
         return out

@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -214,6 +215,72 @@ extern "C" int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int 
         case PA_IN_BF16: e = pa::launch_attn_bf16(h->head_dim, a, s); break;
         default: e = pa::launch_attn_i16(h->head_dim, a, s); break;
     }
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+namespace {
+
+constexpr int kDecodeCUs = 256;
+constexpr int kDecodeMinKeysPerSplit = 256;
+
+size_t decode_ws_bytes(const prefill_attn* h, int batch, int n_split) {
+    return static_cast<size_t>(batch) * h->n_heads * n_split * (h->head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" size_t prefill_attn_decode_workspace_size(const prefill_attn* h, int batch, int n_split) {
+    if (!h || batch < 0 || n_split < 1) return 0;
+    return n_split == 1 ? 0 : decode_ws_bytes(h, batch, n_split);
+}
+
+extern "C" int prefill_attn_decode(const prefill_attn* h, int in_dtype, int batch, const void* q,
+                                   const void* k_cache, const void* v_cache, int n_slots, const int32_t* kv_map,
+                                   int map_stride, const int32_t* pos_offsets, float* out, float score_scale,
+                                   int n_split, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!h || batch < 0 || n_split < 0) return PA_EINVAL;
+    if (in_dtype != PA_IN_F32 && in_dtype != PA_IN_BF16) return PA_EINVAL;
+    if (!std::isfinite(score_scale)) return PA_EINVAL;
+    if (pos_offsets && !aligned4(pos_offsets)) return PA_EINVAL;
+    if (batch == 0) return PA_OK;
+    const int el = in_dtype == PA_IN_F32 ? 4 : 2;
+    int rc = check_cache(h, el, 1, n_slots, kv_map, map_stride, k_cache, v_cache);
+    if (rc != PA_OK) return rc;
+    if (!q || !out || !aligned16(q) || !aligned16(out)) return PA_EINVAL;
+    if (workspace && !aligned16(workspace)) return PA_EINVAL;
+
+    const int G = pa::decode_group(h->n_heads, h->n_kv_heads);
+    const int groups = batch * (h->n_heads / G);
+    if (n_split == 0) {
+        // One full round of resident workgroups: four per CU (two for eight heads per group).
+        const int target = kDecodeCUs * (G >= 8 ? 2 : 4);
+        n_split = std::max(1, target / groups);
+        n_split = std::min(n_split, std::max(1, map_stride / kDecodeMinKeysPerSplit));
+    }
+    if (n_split > 1 && (!workspace || workspace_bytes < decode_ws_bytes(h, batch, 2))) n_split = 1;
+    while (n_split > 1 && decode_ws_bytes(h, batch, n_split) > workspace_bytes) --n_split;
+
+    pa::DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.kv_map = kv_map;
+    a.pos_offsets = pos_offsets;
+    a.out = out;
+    a.rope_f32 = h->d_rope_f32;
+    a.status = h->d_status;
+    a.ws = static_cast<float*>(workspace);
+    a.batch = batch;
+    a.n_heads = h->n_heads;
+    a.n_kv_heads = h->n_kv_heads;
+    a.max_seq = h->max_seq;
+    a.map_stride = map_stride;
+    a.n_slots = n_slots;
+    a.n_split = n_split;
+    const float scale = score_scale != 0.0f ? score_scale : 1.0f / std::sqrt(static_cast<float>(h->head_dim));
+    a.logit_scale = scale * 1.44269504088896340736f;
+    hipError_t e = pa::launch_decode(h->head_dim, in_dtype == PA_IN_F32, a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 

@@ -39,6 +39,31 @@ hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t stream);
 hipError_t launch_kv_cache_update(int head_dim, int el, const RunArgs& a, void* dst_k, void* dst_v,
                                   hipStream_t stream);
 
+// Decode attention (one new token per sequence) against a KV cache.
+struct DecodeArgs {
+    const void* q;               // [batch][n_heads][D]
+    const void* k;               // caches [n_slots][n_kv_heads][D]
+    const void* v;
+    const int32_t* kv_map;       // [batch][map_stride] logical position -> slot
+    const int32_t* pos_offsets;  // [batch] position of the new token (may be null: 0)
+    float* out;                  // [batch][n_heads][D]
+    const float* rope_f32;
+    int* status;
+    float* ws;                   // n_split > 1: partial O, then (max, sum) pairs
+    int batch;
+    int n_heads;
+    int n_kv_heads;
+    int max_seq;
+    int map_stride;
+    int n_slots;
+    int n_split;
+    float logit_scale;           // score_scale * log2(e)
+};
+
+// Query heads served by one decode workgroup (a divisor of n_heads / n_kv_heads).
+int decode_group(int n_heads, int n_kv_heads);
+hipError_t launch_decode(int head_dim, bool f32, const DecodeArgs& a, hipStream_t stream);
+
 // Int16 test exports; RunArgs.q is the tensor to rotate (x) for the rope one,
 // q/k for the scores one; `dst` receives int16 x_rot or int32 scores.
 hipError_t launch_debug_rope_i16(int head_dim, const RunArgs& a, int n_heads_x, int16_t* dst,

@@ -95,6 +95,9 @@ def test_calls_on_null_handle():
                                             None) == pa.PA_EINVAL
     assert lib.prefill_attn_run_cached(None, pa.PA_IN_BF16, 1, 4, 16, 16, 16, 8, 16, 4, None, 16, 0.0,
                                        None) == pa.PA_EINVAL
+    assert lib.prefill_attn_decode(None, pa.PA_IN_BF16, 1, 16, 16, 16, 8, 16, 4, None, 16, 0.0, 0, None, 0,
+                                   None) == pa.PA_EINVAL
+    assert lib.prefill_attn_decode_workspace_size(None, 4, 8) == 0
 
 
 @pytest.mark.parametrize("n_slots,start,count", [(128, 120, 12), (8, 0, 8), (5, 4, 23), (1, 0, 3), (16, 3, 0)])
