@@ -22,13 +22,15 @@ Pages cited (by title and section):
 * "手写内核实现6倍prefill加速" §2.2 and §3.2 again for the KV cache: new
   tokens' K/V copied into free slots, an index map from logical position to
   physical slot (``kv_cache.py``).
+* the 2kiu.com retelling, §3.3, and the MNN-on-K3 blog, §四, for the
+  per-token dynamic int16 quantisation of float Q/K (``quantize.py``).
 
 The blocked online softmax of those pages reaches, in exact arithmetic, the
 plain causal softmax-attention result; so this oracle is that plain
 definition: explicit RoPE, the full causal score matrix, a two-pass softmax.
 
-Parity pins (tests/test_oracle_pins.py, tests/test_oracle_cache_pins.py)
-cover every function here; none is
+Parity pins (tests/test_oracle_pins.py, tests/test_oracle_cache_pins.py,
+tests/test_oracle_quant_pins.py) cover every function here; none is
 "parity unpinned".  Two *inputs* are readings rather than derivations and are
 documented as such with the workloads: the int16 ``score_scale`` and the
 per-head scale recipe of the long-prompt workload.
@@ -50,6 +52,11 @@ from .kv_cache import (
     attention_cached,
     attention_cached_rows,
     attention_i16_cached,
+)
+from .quantize import (
+    quantize_rows_i16,
+    attention_i16_quantized,
+    attention_i16_quantized_rows,
 )
 from .fixed_point import (
     rope_table_q14,
@@ -78,4 +85,7 @@ __all__ = [
     "attention_cached",
     "attention_cached_rows",
     "attention_i16_cached",
+    "quantize_rows_i16",
+    "attention_i16_quantized",
+    "attention_i16_quantized_rows",
 ]
