@@ -50,11 +50,11 @@ def kernel_sha():
 
 def algorithmic_bytes(w):
     """Q, K, V read once, O (fp32) written once, RoPE table rows read once."""
-    el = {"f32": 4, "bf16": 2, "i16": 2}[w.dtype]
+    el = {"f32": 4, "bf16": 2, "i16": 2, "bf16q": 2}[w.dtype]
     q = w.batch * w.seq_len * w.n_heads * w.head_dim * el
     kv = 2 * w.batch * w.seq_len * w.n_kv_heads * w.head_dim * (el if w.dtype != "i16" else 2)
     o = w.batch * w.seq_len * w.n_heads * w.head_dim * 4
-    tab = w.seq_len * w.head_dim * (4 if w.dtype != "i16" else 2)
+    tab = w.seq_len * w.head_dim * (2 if w.dtype in ("i16", "bf16q") else 4)  # Q1.14 or fp32 pairs
     return q + kv + o + tab
 
 
@@ -92,7 +92,10 @@ def cpu_baseline(w, budget_s):
     for h in range(w.n_heads):
         qs, ks, vs = q[:1, :, h:h + 1], k[:1, :, h // g:h // g + 1], v[:1, :, h // g:h // g + 1]
         t0 = time.perf_counter()
-        if w.dtype == "i16":
+        if w.dtype == "bf16q":
+            oracle.attention_i16_quantized(qs.float().numpy(), ks.float().numpy(), synth.to_f64(vs),
+                                           rope_theta=w.rope_theta, score_scale=w.score_scale or None)
+        elif w.dtype == "i16":
             oracle.attention_i16(synth.to_f64(qs), synth.to_f64(ks), synth.to_f64(vs), rope_theta=w.rope_theta,
                                  score_scale=one.score_scale)
         else:
@@ -210,7 +213,7 @@ def main():
 
     if args.mode == "prefill":
         def step():
-            attn(qd, kd, vd, score_scale=w.score_scale, out=out, stream=stream)
+            attn(qd, kd, vd, score_scale=w.score_scale, out=out, stream=stream, quantize=w.dtype == "bf16q")
     else:
         # Ring cache of seq_len slots starting at slot 1000 (wraps), one map row per sequence.
         S, B = w.seq_len, w.batch
@@ -279,7 +282,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if w.dtype == "bf16" else {"f32": "f32", "i16": "i8"}[w.dtype],
+        "dtype": "f16" if w.dtype == "bf16" else {"f32": "f32", "i16": "i8", "bf16q": "i8"}[w.dtype],
         "data": "synthetic",
         "config": {
             "workload": w.name if args.mode == "prefill" else f"{w.name}, chunked prefill in chunks of {args.chunk}",

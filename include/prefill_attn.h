@@ -55,7 +55,11 @@ typedef struct prefill_attn prefill_attn; /* opaque handle */
 enum prefill_attn_dtype {
     PA_IN_F32 = 0,  /* Q, K, V float32; products on the fp32 matrix cores */
     PA_IN_BF16 = 1, /* Q, K, V bfloat16; rotated Q'/K', P and V rounded to fp16 for the matrix cores, fp32 accumulate */
-    PA_IN_I16 = 2   /* Q, K int16 fixed point, V bfloat16; integer RoPE, exact int32 scores, fp32 softmax */
+    PA_IN_I16 = 2,  /* Q, K int16 fixed point, V bfloat16; integer RoPE, exact int32 scores, fp32 softmax */
+    PA_IN_BF16_Q16 = 3 /* Q, K, V bfloat16; each (token, head) row of Q and K quantised inside the kernel to
+                          int16 codes, round-half-even(x * 2047 / max|x|) in fp32 (the 2kiu.com retelling, §3.3:
+                          per-token dynamic activation scale), then the PA_IN_I16 path with
+                          logit = (int32 score) * score_scale * (max|q| / 2047) * (max|k| / 2047) */
 };
 
 enum prefill_attn_status {
@@ -93,7 +97,8 @@ int prefill_attn_init(prefill_attn** out, int n_heads, int n_kv_heads, int head_
  *   pos_offsets  device int32[batch], or NULL for all zeros
  *   out          device float32 O; every element of rows i < seq_len is written
  *   score_scale  multiplies the score: PA_IN_F32/PA_IN_BF16 logit = (Q'.K') * score_scale,
- *                PA_IN_I16 logit = (int32 score) * score_scale; 0 selects 1/sqrt(head_dim)
+ *                PA_IN_I16 logit = (int32 score) * score_scale, PA_IN_BF16_Q16 as documented
+ *                with the enum; 0 selects 1/sqrt(head_dim)
  * A batch element whose positions leave [0, max_seq) gets O = 0 and sets the
  * handle's status word (read it with prefill_attn_status).  Runs on one handle
  * may overlap on several streams; they share only that status word.
@@ -241,6 +246,11 @@ int prefill_attn_debug_rope_i16(const prefill_attn* h, int batch, int seq_len,
                                 int16_t* x_rot, void* stream);
 int prefill_attn_debug_scores_i32(const prefill_attn* h, int batch, int seq_len,
                                   const int16_t* q, const int16_t* k, const int32_t* pos_offsets,
+                                  int32_t* scores, void* stream);
+/* The same score matrix for bfloat16 Q/K through the in-kernel quantisation of
+ * PA_IN_BF16_Q16: scores of the int16 codes. */
+int prefill_attn_debug_scores_q16(const prefill_attn* h, int batch, int seq_len,
+                                  const void* q, const void* k, const int32_t* pos_offsets,
                                   int32_t* scores, void* stream);
 
 #ifdef __cplusplus

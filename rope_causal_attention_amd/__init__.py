@@ -18,18 +18,18 @@ import numpy as np
 import torch
 
 __all__ = [
-    "PA_IN_F32", "PA_IN_BF16", "PA_IN_I16",
+    "PA_IN_F32", "PA_IN_BF16", "PA_IN_I16", "PA_IN_BF16_Q16",
     "PA_OK", "PA_EINVAL", "PA_ENOMEM", "PA_EDEVICE", "PA_ELAUNCH", "PA_ERANGE",
     "PrefillAttnError", "load_library", "library_path",
     "prefill_attn_init", "prefill_attn_run", "prefill_attn_status", "prefill_attn_destroy",
     "prefill_attn_strerror", "prefill_attn_rope_table_f32", "prefill_attn_rope_table_q14",
-    "prefill_attn_debug_rope_i16", "prefill_attn_debug_scores_i32",
+    "prefill_attn_debug_rope_i16", "prefill_attn_debug_scores_i32", "prefill_attn_debug_scores_q16",
     "prefill_attn_kv_cache_update", "prefill_attn_run_cached", "prefill_attn_ring_map", "prefill_attn_paged_map",
     "prefill_attn_decode", "prefill_attn_decode_workspace_size",
     "PrefillAttention", "EXPORTED_SYMBOLS",
 ]
 
-PA_IN_F32, PA_IN_BF16, PA_IN_I16 = 0, 1, 2
+PA_IN_F32, PA_IN_BF16, PA_IN_I16, PA_IN_BF16_Q16 = 0, 1, 2, 3
 PA_OK, PA_EINVAL, PA_ENOMEM, PA_EDEVICE, PA_ELAUNCH, PA_ERANGE = 0, -1, -2, -3, -4, -5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,6 +47,7 @@ _SIGNATURES = {
     "prefill_attn_rope_table_q14": (_I, [_I, _I, ctypes.c_double, _P]),
     "prefill_attn_debug_rope_i16": (_I, [_P, _I, _I, _P, _I, _P, _P, _P]),
     "prefill_attn_debug_scores_i32": (_I, [_P, _I, _I, _P, _P, _P, _P, _P]),
+    "prefill_attn_debug_scores_q16": (_I, [_P, _I, _I, _P, _P, _P, _P, _P]),
     "prefill_attn_kv_cache_update": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _I, _P]),
     "prefill_attn_run_cached": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _P]),
     "prefill_attn_ring_map": (_I, [_I, _I, _I, _P]),
@@ -191,6 +192,12 @@ def prefill_attn_debug_scores_i32(handle, batch, seq_len, q, k, pos_offsets, sco
            "prefill_attn_debug_scores_i32")
 
 
+def prefill_attn_debug_scores_q16(handle, batch, seq_len, q, k, pos_offsets, scores, stream=None):
+    _check(load_library().prefill_attn_debug_scores_q16(handle, batch, seq_len, _ptr(q), _ptr(k),
+                                                        _ptr(pos_offsets), _ptr(scores), _stream(stream)),
+           "prefill_attn_debug_scores_q16")
+
+
 def prefill_attn_kv_cache_update(handle, in_dtype, batch, seq_len, k_new, v_new, pos_offsets, kv_map, map_stride,
                                  k_cache, v_cache, n_slots, stream=None):
     """Copy the new tokens' K/V into their cache slots (see the header)."""
@@ -269,10 +276,18 @@ class PrefillAttention:
         except Exception:  # noqa: BLE001 - interpreter shutdown
             pass
 
-    def _validate(self, q, k, v, pos_offsets, out):
+    @staticmethod
+    def _dtype(q, quantize):
         if q.dtype not in _DTYPES:
             raise TypeError(f"unsupported q dtype {q.dtype}")
-        dt = _DTYPES[q.dtype]
+        if quantize:
+            if q.dtype != torch.bfloat16:
+                raise TypeError("quantize=True takes bfloat16 q/k/v")
+            return PA_IN_BF16_Q16
+        return _DTYPES[q.dtype]
+
+    def _validate(self, q, k, v, pos_offsets, out, quantize=False):
+        dt = self._dtype(q, quantize)
         want_kv = q.dtype
         if k.dtype != want_kv or v.dtype != (torch.bfloat16 if dt == PA_IN_I16 else want_kv):
             raise TypeError("k must match q's dtype; v must too (bfloat16 for int16 q/k)")
@@ -291,8 +306,10 @@ class PrefillAttention:
             raise ValueError("pos_offsets must be a device int32 tensor with one entry per batch element")
         return dt, B, S
 
-    def __call__(self, q, k, v, pos_offsets=None, score_scale=0.0, out=None, stream=None):
-        dt, B, S = self._validate(q, k, v, pos_offsets, out)
+    def __call__(self, q, k, v, pos_offsets=None, score_scale=0.0, out=None, stream=None, quantize=False):
+        """O (float32) of q [B][S][Hq][D], k/v [B][S][Hkv][D].  quantize=True runs bfloat16
+        inputs through the in-kernel per-token int16 quantisation (PA_IN_BF16_Q16)."""
+        dt, B, S = self._validate(q, k, v, pos_offsets, out, quantize)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         prefill_attn_run(self.handle, dt, B, S, q, k, v, pos_offsets, out, score_scale, stream)
@@ -308,7 +325,8 @@ class PrefillAttention:
             raise ValueError("caches must be [n_slots][n_kv_heads][head_dim]")
         if tuple(v_cache.shape) != tuple(k_cache.shape):
             raise ValueError("k_cache and v_cache must have the same shape")
-        if k_cache.dtype != {PA_IN_F32: torch.float32, PA_IN_BF16: torch.bfloat16, PA_IN_I16: torch.int16}[dt] or \
+        if k_cache.dtype != {PA_IN_F32: torch.float32, PA_IN_BF16: torch.bfloat16, PA_IN_I16: torch.int16,
+                             PA_IN_BF16_Q16: torch.bfloat16}[dt] or \
                 v_cache.dtype != (torch.bfloat16 if dt == PA_IN_I16 else k_cache.dtype):
             raise TypeError("cache dtypes must match the inputs (int16 K with bfloat16 V for the int16 variant)")
         if kv_map.dtype != torch.int32 or kv_map.dim() != 2 or kv_map.shape[0] != B:
@@ -332,12 +350,11 @@ class PrefillAttention:
         prefill_attn_kv_cache_update(self.handle, dt, B, S, k_new, v_new, pos_offsets, kv_map, stride, k_cache,
                                      v_cache, n_slots, stream)
 
-    def run_cached(self, q, k_cache, v_cache, kv_map, pos_offsets=None, score_scale=0.0, out=None, stream=None):
+    def run_cached(self, q, k_cache, v_cache, kv_map, pos_offsets=None, score_scale=0.0, out=None, stream=None,
+                   quantize=False):
         """Chunked prefill: queries q [B][S][Hq][D] at positions pos_offsets[b] + i
         against the cached logical keys 0 .. pos_offsets[b] + i.  Returns O (float32)."""
-        dt = _DTYPES.get(q.dtype)
-        if dt is None:
-            raise TypeError(f"unsupported q dtype {q.dtype}")
+        dt = self._dtype(q, quantize)
         B, S, Hq, D = q.shape
         if Hq != self.n_heads or D != self.head_dim or not q.is_cuda or not q.is_contiguous():
             raise ValueError("q must be a contiguous device tensor [B][S][n_heads][head_dim]")

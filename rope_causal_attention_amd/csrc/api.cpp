@@ -120,7 +120,8 @@ extern "C" int prefill_attn_run(const prefill_attn* h, int in_dtype, int batch, 
     pa::RunArgs a;
     const int rc = prepare(h, batch, seq_len, pos_offsets, a);
     if (rc != PA_OK) return rc;
-    if (in_dtype != PA_IN_F32 && in_dtype != PA_IN_BF16 && in_dtype != PA_IN_I16) return PA_EINVAL;
+    if (in_dtype != PA_IN_F32 && in_dtype != PA_IN_BF16 && in_dtype != PA_IN_I16 && in_dtype != PA_IN_BF16_Q16)
+        return PA_EINVAL;
     if (!std::isfinite(score_scale)) return PA_EINVAL;
     if (batch == 0 || seq_len == 0) return PA_OK;
     if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -135,6 +136,7 @@ extern "C" int prefill_attn_run(const prefill_attn* h, int in_dtype, int batch, 
     switch (in_dtype) {
         case PA_IN_F32: e = pa::launch_attn_f32(h->head_dim, a, s); break;
         case PA_IN_BF16: e = pa::launch_attn_bf16(h->head_dim, a, s); break;
+        case PA_IN_BF16_Q16: e = pa::launch_attn_i16q(h->head_dim, a, s); break;
         default: e = pa::launch_attn_i16(h->head_dim, a, s); break;
     }
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
@@ -147,6 +149,7 @@ int elem_bytes(int in_dtype) {
         case PA_IN_F32: return 4;
         case PA_IN_BF16: return 2;
         case PA_IN_I16: return 2;  // int16 K, bf16 V
+        case PA_IN_BF16_Q16: return 2;
         default: return 0;
     }
 }
@@ -213,6 +216,7 @@ extern "C" int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int 
     switch (in_dtype) {
         case PA_IN_F32: e = pa::launch_attn_f32(h->head_dim, a, s); break;
         case PA_IN_BF16: e = pa::launch_attn_bf16(h->head_dim, a, s); break;
+        case PA_IN_BF16_Q16: e = pa::launch_attn_i16q(h->head_dim, a, s); break;
         default: e = pa::launch_attn_i16(h->head_dim, a, s); break;
     }
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
@@ -347,9 +351,9 @@ extern "C" int prefill_attn_debug_rope_i16(const prefill_attn* h, int batch, int
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
-extern "C" int prefill_attn_debug_scores_i32(const prefill_attn* h, int batch, int seq_len, const int16_t* q,
-                                             const int16_t* k, const int32_t* pos_offsets, int32_t* scores,
-                                             void* stream) {
+namespace {
+int debug_scores(const prefill_attn* h, bool quant, int batch, int seq_len, const void* q, const void* k,
+                 const int32_t* pos_offsets, int32_t* scores, void* stream) {
     pa::RunArgs a;
     const int rc = prepare(h, batch, seq_len, pos_offsets, a);
     if (rc != PA_OK) return rc;
@@ -357,6 +361,20 @@ extern "C" int prefill_attn_debug_scores_i32(const prefill_attn* h, int batch, i
     if (!q || !k || !scores || !aligned16(q) || !aligned16(k) || !aligned16(scores)) return PA_EINVAL;
     a.q = q;
     a.k = k;
-    hipError_t e = pa::launch_debug_scores_i32(h->head_dim, a, scores, static_cast<hipStream_t>(stream));
+    hipError_t e = quant ? pa::launch_debug_scores_q16(h->head_dim, a, scores, static_cast<hipStream_t>(stream))
+                         : pa::launch_debug_scores_i32(h->head_dim, a, scores, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+}  // namespace
+
+extern "C" int prefill_attn_debug_scores_q16(const prefill_attn* h, int batch, int seq_len, const void* q,
+                                             const void* k, const int32_t* pos_offsets, int32_t* scores,
+                                             void* stream) {
+    return debug_scores(h, true, batch, seq_len, q, k, pos_offsets, scores, stream);
+}
+
+extern "C" int prefill_attn_debug_scores_i32(const prefill_attn* h, int batch, int seq_len, const int16_t* q,
+                                             const int16_t* k, const int32_t* pos_offsets, int32_t* scores,
+                                             void* stream) {
+    return debug_scores(h, false, batch, seq_len, q, k, pos_offsets, scores, stream);
 }

@@ -566,6 +566,175 @@ struct I16QK {
     }
 };
 
+// ------------------------------------------------ Q.K^T policy: bf16 inputs quantised in-kernel
+
+// Per-token dynamic int16 quantisation (the 2kiu.com retelling, §3.3): each
+// (token, head) row of Q and K is scaled by 2047 / max|x| and rounded half to
+// even, all in fp32, so every workgroup that stages a row derives the same
+// codes; the MNN-on-K3 blog (§四) fuses the absmax scan with the quantise
+// step, done here while the row is in registers.  The codes then take the
+// int16 path (integer RoPE, three-digit exact int32 scores); the logit is
+// s * score_scale * (m_q / 2047) * (m_k / 2047).
+__device__ __forceinline__ float quant_scale(float m) { return m > 0.f ? 2047.0f / m : 0.f; }
+__device__ __forceinline__ int quant_code(float x, float scale) {
+    return static_cast<int>(fminf(fmaxf(__builtin_rintf(x * scale), -2048.f), 2047.f));
+}
+// Max over the 16 lanes of a DPP row (every lane receives it).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+    return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+}
+
+template <int D, int NT>
+struct I16QuantQK : I16QK<D, NT> {
+    using Base = I16QK<D, NT>;
+    static constexpr int kRow = Base::kRow;
+    static constexpr int kPlane = Base::kPlane;
+    static constexpr int kInv = 3 * kPlane;            // 64 floats: m_k / 2047 of each key row
+    static constexpr int kBytes = 3 * kPlane + BN * 4;
+    static constexpr int E = D / 16;                   // elements of a key row per lane (16 lanes per row)
+    static constexpr int kPasses = BN * 16 / NT;       // rows per thread per tile
+    static_assert(BN * 16 % NT == 0, "whole passes");
+    using Q = typename Base::Q;
+    using KPtr = typename Base::KPtr;
+    struct KRegs {
+        uint32_t raw[kPasses][E / 2];  // bf16 pairs
+        uint32_t cs[kPasses][E / 2];   // Q1.14 (C, S) pairs
+    };
+
+    template <bool MAPPED>
+    __device__ static __forceinline__ KPtr kptr(const RunArgs& a, const Ctx& c) {
+        return Base::template kptr<MAPPED>(a, c);
+    }
+
+    // Q: the lane holds dims 32 ks + 16 lh .. +15 of query qi; the row max
+    // comes from both lane halves.
+    __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
+        const int lh = (threadIdx.x & 63) >> 5;
+        const bool ok = qi < c.S;
+        const Rows rq = q_rows(a, c, a.q, D, 2);
+        const char* tab = reinterpret_cast<const char*>(a.rope_q14 + static_cast<size_t>(c.off) * D);
+        uint4 raw[D / 32][2], cs[D / 32][2];
+        float m = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int d0 = 32 * ks + 16 * lh + 8 * half;
+                raw[ks][half] = ok ? ld16(rq.base, qi * rq.stride + 2 * d0) : make_uint4(0, 0, 0, 0);
+                cs[ks][half] = ok ? ld16(tab, (qi * D + d0) * 2) : make_uint4(0, 0, 0, 0);
+                const uint32_t w[4] = {raw[ks][half].x, raw[ks][half].y, raw[ks][half].z, raw[ks][half].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf_lo(w[j])), fabsf(bf_hi(w[j]))));
+            }
+        m = halves_max(m);
+        const float qs = quant_scale(m);
+        q.scale = scale * (m / 2047.0f);
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            uint2 h[2], l[2], mm[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const uint32_t w[4] = {raw[ks][half].x, raw[ks][half].y, raw[ks][half].z, raw[ks][half].w};
+                uint32_t cw[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    cw[j] = (static_cast<uint32_t>(quant_code(bf_lo(w[j]), qs)) & 0xffffu) |
+                            (static_cast<uint32_t>(quant_code(bf_hi(w[j]), qs)) << 16);
+                Base::rotate_split8(make_uint4(cw[0], cw[1], cw[2], cw[3]), cs[ks][half], h[half], l[half], mm[half]);
+            }
+            q.h[ks] = i32x4{(int)h[0].x, (int)h[0].y, (int)h[1].x, (int)h[1].y};
+            q.l[ks] = i32x4{(int)l[0].x, (int)l[0].y, (int)l[1].x, (int)l[1].y};
+            q.m[ks] = i32x4{(int)mm[0].x, (int)mm[0].y, (int)mm[1].x, (int)mm[1].y};
+        }
+    }
+
+    // K: 16 lanes per key row, lane sub holds elements [E sub, E sub + E).
+    template <bool CLAMP, bool MAPPED>
+    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
+        const int tid = threadIdx.x % NT;
+        const int sub = tid & 15;
+        const char* kb = p.k.template tile_base<MAPPED>(tile);
+        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+            int row = (tid >> 4) + (NT / 16) * i;
+            if (CLAMP) row = min(row, p.S - 1 - tile * BN);
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(kb + p.k.template row_off<MAPPED>(tile, row) + 2 * E * sub);
+            const uint32_t* t = reinterpret_cast<const uint32_t*>(tb + (row * D + E * sub) * 2);
+#pragma unroll
+            for (int e = 0; e < E / 2; ++e) {
+                r.raw[i][e] = src[e];
+                r.cs[i][e] = t[e];
+            }
+        }
+    }
+
+    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
+        const int tid = threadIdx.x % NT;
+        const int sub = tid & 15;
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+            const int row = (tid >> 4) + (NT / 16) * i;
+            float m = 0.f;
+#pragma unroll
+            for (int e = 0; e < E / 2; ++e) m = fmaxf(m, fmaxf(fabsf(bf_lo(r.raw[i][e])), fabsf(bf_hi(r.raw[i][e]))));
+            m = row_max16(m);
+            const float ks = quant_scale(m);
+            uint32_t hb[E / 4 + 1] = {}, lb[E / 4 + 1] = {}, mb[E / 4 + 1] = {};
+#pragma unroll
+            for (int e = 0; e < E / 2; ++e) {
+                const int x = quant_code(bf_lo(r.raw[i][e]), ks), y = quant_code(bf_hi(r.raw[i][e]), ks);
+                const int C = i16_lo(r.cs[i][e]), S = i16_hi(r.cs[i][e]);
+                uint32_t a0, a1, a2, b0, b1, b2;
+                Base::split(Base::rot_x(x, y, C, S), a0, a1, a2);
+                Base::split(Base::rot_y(x, y, C, S), b0, b1, b2);
+                const int sh = 16 * (e & 1);
+                hb[e >> 1] |= (a0 | (b0 << 8)) << sh;
+                lb[e >> 1] |= (a1 | (b1 << 8)) << sh;
+                mb[e >> 1] |= (a2 | (b2 << 8)) << sh;
+            }
+            char* pr = lds + row * kRow + E * sub;
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) {
+                const uint32_t* w = pl == 0 ? hb : pl == 1 ? lb : mb;
+                char* dst = pr + pl * kPlane;
+                if (E == 8) {
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+                } else if (E == 4) {
+                    *reinterpret_cast<uint32_t*>(dst) = w[0];
+                } else {  // E == 6: six bytes at a 2-byte aligned offset
+                    *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(w[0]);
+                    *reinterpret_cast<uint16_t*>(dst + 2) = static_cast<uint16_t>(w[0] >> 16);
+                    *reinterpret_cast<uint16_t*>(dst + 4) = static_cast<uint16_t>(w[1]);
+                }
+            }
+            if (sub == 0) reinterpret_cast<float*>(lds + kInv)[row] = m / 2047.0f;
+        }
+    }
+
+    // Logits (log2 units): float(score) * scale_q * m_k / 2047 of each key.
+    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh) {
+        int si[16];
+        Base::qk_i32(lds, kb, q, si, lq, lh);
+        const float* inv = reinterpret_cast<const float*>(lds + kInv) + 32 * kb + 4 * lh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 f = *reinterpret_cast<const float4*>(inv + 8 * g);
+            s[4 * g + 0] = static_cast<float>(si[4 * g + 0]) * q.scale * f.x;
+            s[4 * g + 1] = static_cast<float>(si[4 * g + 1]) * q.scale * f.y;
+            s[4 * g + 2] = static_cast<float>(si[4 * g + 2]) * q.scale * f.z;
+            s[4 * g + 3] = static_cast<float>(si[4 * g + 3]) * q.scale * f.w;
+        }
+    }
+};
+
 // ------------------------------------------------ balanced staging for 8 waves
 
 // With 512 threads every thread stages the same amount of a 64-key tile, so
@@ -1045,10 +1214,11 @@ __global__ __launch_bounds__(kThreads) void debug_rope_i16_kernel(RunArgs a, int
     dst[2 * pair + 1] = static_cast<int16_t>(I16QK<D, kThreads>::rot_y(x, y, t[0], t[1]));
 }
 
-// Full (unmasked) int32 score matrix through the same staging and MFMA code.
-template <int D>
+// Full (unmasked) int32 score matrix through the same staging and MFMA code
+// (int16 inputs, or bf16 inputs quantised in-kernel).
+template <int D, template <int, int> class QKT>
 __global__ __launch_bounds__(kThreads) void debug_scores_i32_kernel(RunArgs a, int32_t* dst) {
-    using P = I16QK<D, kThreads>;
+    using P = QKT<D, kThreads>;
     __shared__ __attribute__((aligned(16))) char lds[P::kBytes];
     Ctx c;
     if (!make_ctx<BM, false>(a, c)) {
@@ -1114,16 +1284,20 @@ hipError_t launch_bf16_d(const RunArgs& a, hipStream_t s) {
         launch_bf16_dm<D, false>(a, s);
     return hipGetLastError();
 }
-template <int D>
-hipError_t launch_i16_d(const RunArgs& a, hipStream_t s) {
+template <int D, template <int, int> class QKT>
+hipError_t launch_int_d(const RunArgs& a, hipStream_t s) {
     if (a.kv_map)
-        hipLaunchKernelGGL((attn_fwd_kernel<D, I16QK, VStage, 4, 1, true>), grid_for(a, 128), dim3(256), 0, s, a,
+        hipLaunchKernelGGL((attn_fwd_kernel<D, QKT, VStage, 4, 1, true>), grid_for(a, 128), dim3(256), 0, s, a,
                            a.score_scale * kLog2e);
     else
-        hipLaunchKernelGGL((attn_fwd_kernel<D, I16QK, VStage, 4, 1, false>), grid_for(a, 128), dim3(256), 0, s, a,
+        hipLaunchKernelGGL((attn_fwd_kernel<D, QKT, VStage, 4, 1, false>), grid_for(a, 128), dim3(256), 0, s, a,
                            a.score_scale * kLog2e);
     return hipGetLastError();
 }
+template <int D>
+hipError_t launch_i16_d(const RunArgs& a, hipStream_t s) { return launch_int_d<D, I16QK>(a, s); }
+template <int D>
+hipError_t launch_i16q_d(const RunArgs& a, hipStream_t s) { return launch_int_d<D, I16QuantQK>(a, s); }
 template <int D>
 hipError_t launch_f32_d(const RunArgs& a, hipStream_t s) {
     if (a.kv_map)
@@ -1147,6 +1321,7 @@ hipError_t launch_f32_d(const RunArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_bf16_d, head_dim, a, s) }
 hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_i16_d, head_dim, a, s) }
+hipError_t launch_attn_i16q(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_i16q_d, head_dim, a, s) }
 hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_f32_d, head_dim, a, s) }
 
 hipError_t launch_kv_cache_update(int head_dim, int el, const RunArgs& a, void* dst_k, void* dst_v, hipStream_t s) {
@@ -1172,7 +1347,12 @@ hipError_t launch_rope_d(const RunArgs& a, int n_heads_x, int16_t* dst, hipStrea
 }
 template <int D>
 hipError_t launch_scores_d(const RunArgs& a, int32_t* dst, hipStream_t s) {
-    hipLaunchKernelGGL((debug_scores_i32_kernel<D>), grid_for(a, BM), dim3(kThreads), 0, s, a, dst);
+    hipLaunchKernelGGL((debug_scores_i32_kernel<D, I16QK>), grid_for(a, BM), dim3(kThreads), 0, s, a, dst);
+    return hipGetLastError();
+}
+template <int D>
+hipError_t launch_scores_q_d(const RunArgs& a, int32_t* dst, hipStream_t s) {
+    hipLaunchKernelGGL((debug_scores_i32_kernel<D, I16QuantQK>), grid_for(a, BM), dim3(kThreads), 0, s, a, dst);
     return hipGetLastError();
 }
 }  // namespace
@@ -1182,6 +1362,9 @@ hipError_t launch_debug_rope_i16(int head_dim, const RunArgs& a, int n_heads_x, 
 }
 hipError_t launch_debug_scores_i32(int head_dim, const RunArgs& a, int32_t* dst, hipStream_t s) {
     PA_DISPATCH_D(launch_scores_d, head_dim, a, dst, s)
+}
+hipError_t launch_debug_scores_q16(int head_dim, const RunArgs& a, int32_t* dst, hipStream_t s) {
+    PA_DISPATCH_D(launch_scores_q_d, head_dim, a, dst, s)
 }
 
 }  // namespace pa

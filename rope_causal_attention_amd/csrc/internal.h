@@ -33,6 +33,8 @@ struct RunArgs {
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t stream);
 hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t stream);
+// bf16 Q/K quantised in-kernel per (token, head) row to int16, then the int16 path.
+hipError_t launch_attn_i16q(int head_dim, const RunArgs& a, hipStream_t stream);
 
 // Copies the new tokens' K/V ([batch][seq_len][n_kv_heads][D], `el` bytes per
 // element) into their cache slots; a.k/a.v are the new K/V, dst_k/dst_v the caches.
@@ -69,5 +71,6 @@ hipError_t launch_decode(int head_dim, bool f32, const DecodeArgs& a, hipStream_
 hipError_t launch_debug_rope_i16(int head_dim, const RunArgs& a, int n_heads_x, int16_t* dst,
                                  hipStream_t stream);
 hipError_t launch_debug_scores_i32(int head_dim, const RunArgs& a, int32_t* dst, hipStream_t stream);
+hipError_t launch_debug_scores_q16(int head_dim, const RunArgs& a, int32_t* dst, hipStream_t stream);
 
 }  // namespace pa

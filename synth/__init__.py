@@ -16,7 +16,9 @@ Recipe (every workload):
 * one cast to the workload's dtype (bf16 rounds to nearest even; the tiny
   workload stays fp32);
 * the int16 workload draws Q and K as ``randint(-2048, 2048)`` int16 and V as
-  ``randn`` cast to bf16.
+  ``randn`` cast to bf16;
+* dtype "bf16q" draws like "bf16"; it names bf16 inputs that the library
+  quantises to int16 per (token, head) row inside the kernel.
 
 The workloads stand in for the prompts the pages time (a 512-token prompt on
 a 7B model, a pp512 prefill batch on a small GQA model, a long prompt on a
@@ -39,7 +41,7 @@ class Workload:
     n_kv_heads: int
     seq_len: int
     head_dim: int
-    dtype: str              # "f32" | "bf16" | "i16"
+    dtype: str              # "f32" | "bf16" | "i16" | "bf16q"
     rope_theta: float
     seed: int
     head_scale: str = ""    # "" | "independent" | "shared"
@@ -67,6 +69,7 @@ WORKLOADS = {
         Workload("gqa_bf16_b16_h16kv8_s512_d128", 16, 16, 8, 512, 128, "bf16", 1e6, 1004),
         Workload("i16_h32_s2048_d128", 1, 32, 32, 2048, 128, "i16", 1e4, 1005,
                  score_scale=2.0 ** -22 / math.sqrt(128)),
+        Workload("q16_bf16_h32_s2048_d128", 1, 32, 32, 2048, 128, "bf16q", 1e4, 1006),
     ]
 }
 
@@ -96,7 +99,7 @@ def make_inputs(w):
         q = q * sc[0].view(1, 1, Hq, 1)
         k = k * sc[1, :Hkv].view(1, 1, Hkv, 1)
         v = v * sc[2, :Hkv].view(1, 1, Hkv, 1)
-    if w.dtype == "bf16":
+    if w.dtype in ("bf16", "bf16q"):
         q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
     elif w.dtype != "f32":
         raise ValueError(f"unknown dtype {w.dtype}")

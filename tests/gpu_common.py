@@ -54,7 +54,8 @@ def run_gpu(w, q, k, v, pos_offsets=None, score_scale=None, attn=None, max_seq=N
     try:
         qd, kd, vd = to_dev(q, k, v)
         off = None if pos_offsets is None else torch.tensor(pos_offsets, dtype=torch.int32, device="cuda")
-        o = attn(qd, kd, vd, pos_offsets=off, score_scale=w.score_scale if score_scale is None else score_scale)
+        o = attn(qd, kd, vd, pos_offsets=off, score_scale=w.score_scale if score_scale is None else score_scale,
+                 quantize=w.dtype == "bf16q")
         torch.cuda.synchronize()
         assert attn.status() == pa.PA_OK
         return o.cpu()
@@ -64,6 +65,10 @@ def run_gpu(w, q, k, v, pos_offsets=None, score_scale=None, attn=None, max_seq=N
 
 
 def oracle_full(w, q, k, v, pos_offsets=None):
+    if w.dtype == "bf16q":
+        return oracle.attention_i16_quantized(q.float().numpy(), k.float().numpy(), synth.to_f64(v),
+                                              pos_offsets=pos_offsets, rope_theta=w.rope_theta,
+                                              score_scale=w.score_scale or None)
     if w.dtype == "i16":
         return oracle.attention_i16(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), pos_offsets=pos_offsets,
                                     rope_theta=w.rope_theta, score_scale=w.score_scale)
@@ -73,6 +78,10 @@ def oracle_full(w, q, k, v, pos_offsets=None):
 
 
 def oracle_rows(w, q, k, v, rows, pos_offsets=None):
+    if w.dtype == "bf16q":
+        return oracle.attention_i16_quantized_rows(q.float().numpy(), k.float().numpy(), v.float().numpy(), rows,
+                                                   pos_offsets=pos_offsets, rope_theta=w.rope_theta,
+                                                   score_scale=w.score_scale or None)
     if w.dtype == "i16":
         return oracle.attention_i16_rows(q.numpy(), k.numpy(), synth.to_f64(v), rows, pos_offsets=pos_offsets,
                                          rope_theta=w.rope_theta, score_scale=w.score_scale)

@@ -212,3 +212,99 @@ def test_int16_degenerate_scale_small():
     got = run_gpu(w, q, k, v)
     want = oracle_full(w, q, k, v)
     assert_close(got.numpy(), want, "bf16")
+
+
+# ------------------------------------------------------------ bf16 quantised in-kernel to int16
+
+Q16_SCORE_CASES = [
+    # name, B, Hq, Hkv, S, D, offsets
+    ("q16_scores_d128_gqa", 2, 4, 2, 300, 128, [0, 21]),
+    ("q16_scores_d96", 1, 2, 2, 200, 96, [5]),
+    ("q16_scores_d64", 2, 2, 1, 130, 64, None),
+]
+
+
+@pytest.mark.parametrize("case", Q16_SCORE_CASES, ids=[c[0] for c in Q16_SCORE_CASES])
+def test_quantised_scores_bit_exact(case):
+    """The in-kernel codes (fp32 absmax, scale and round-half-even), their integer
+    RoPE and the exact int32 scores, all bit-for-bit against the oracle."""
+    name, B, Hq, Hkv, S, D, offs = case
+    announce(name)
+    w = synth.Workload(name, B, Hq, Hkv, S, D, "bf16q", 1e4, sum(map(ord, name)))
+    q, k, v = synth.make_inputs(w)
+    q[0, 3, 0] = 0  # an all-zero row quantises to zeros
+    max_seq = S + (max(offs) if offs else 0)
+    attn = pa.PrefillAttention(Hq, Hkv, D, max_seq, 1e4)
+    try:
+        qd, kd = to_dev(q, k)
+        od = None if offs is None else torch.tensor(offs, dtype=torch.int32, device="cuda")
+        sc = torch.empty((B, Hq, S, S), dtype=torch.int32, device="cuda")
+        pa.prefill_attn_debug_scores_q16(attn.handle, B, S, qd, kd, od, sc)
+        torch.cuda.synchronize()
+        qc, _ = oracle.quantize_rows_i16(q.float().numpy())
+        kc, _ = oracle.quantize_rows_i16(k.float().numpy())
+        for b in range(B):
+            pos = np.arange(S) + (offs[b] if offs else 0)
+            qr = oracle.rope_rotate_i16(qc[b], pos, 1e4)
+            kr = oracle.rope_rotate_i16(kc[b], pos, 1e4)
+            for h in range(Hq):
+                want = oracle.scores_i32(qr[:, h], kr[:, h // (Hq // Hkv)])
+                got = sc[b, h].cpu().numpy().astype(np.int64)
+                assert np.array_equal(got, want), f"b{b} h{h}: {np.count_nonzero(got != want)} mismatches"
+    finally:
+        attn.close()
+
+
+Q16_SMALL = [
+    # name, B, Hq, Hkv, S, D, offsets
+    ("q16_d128_ragged_gqa", 2, 4, 2, 333, 128, [0, 40]),
+    ("q16_d96_ragged", 1, 4, 4, 257, 96, None),
+    ("q16_d64_s1", 3, 2, 1, 1, 64, None),
+]
+
+
+@pytest.mark.parametrize("case", Q16_SMALL, ids=[c[0] for c in Q16_SMALL])
+def test_quantised_attention_small_full_compare(case):
+    name, B, Hq, Hkv, S, D, offs = case
+    announce(name)
+    max_seq = S + (max(offs) if offs else 0)
+    w = synth.Workload(name, B, Hq, Hkv, S, D, "bf16q", 1e4, sum(map(ord, name)), max_seq=max_seq)
+    q, k, v = synth.make_inputs(w)
+    got = run_gpu(w, q, k, v, pos_offsets=offs)
+    mx, mean = assert_close(got.numpy(), oracle_full(w, q, k, v, pos_offsets=offs), "bf16")
+    announce(name, f"max {mx:.2e} mean {mean:.2e}")
+
+
+def test_quantised_attention_workload():
+    """1 x 32 x 2048 x 128 bf16 through the in-kernel quantisation: two whole heads
+    and rows sampled over all heads."""
+    w = synth.WORKLOADS["q16_bf16_h32_s2048_d128"]
+    announce(w.name)
+    q, k, v = synth.make_inputs(w)
+    got = run_gpu(w, q, k, v).numpy()
+    for h in (0, 31):
+        one = synth.workload(w.name, n_heads=1, n_kv_heads=1)
+        want = oracle_full(one, q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1])
+        assert_close(got[:, :, h:h + 1], want, "bf16")
+    rows = sample_rows(w, 64, seed=13)
+    want = oracle_rows(w, q, k, v, rows)
+    sel = np.stack([got[b, i, h] for b, h, i in rows])
+    mx, _ = errors(sel, want)
+    assert mx <= 1e-2
+
+
+def test_quantised_cached_equals_quantised_prefill_bitwise():
+    w = synth.Workload("q16_cached", 1, 4, 2, 300, 128, "bf16q", 1e4, 4321)
+    announce(w.name)
+    q, k, v = synth.make_inputs(w)
+    attn = pa.PrefillAttention(4, 2, 128, 300, 1e4)
+    try:
+        qd, kd, vd = to_dev(q, k, v)
+        o_plain = attn(qd, kd, vd, quantize=True)
+        ident = torch.arange(300, dtype=torch.int32, device="cuda")[None, :]
+        o_cached = attn.run_cached(qd, kd[0], vd[0], ident, quantize=True)
+        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
+        assert torch.equal(o_plain, o_cached)
+    finally:
+        attn.close()
