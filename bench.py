@@ -14,7 +14,9 @@ with per-head scales, RoPE theta 1e4, causal).  Prints one JSON line.
 --mode chunked prefills the same prompt in chunks of N tokens through a KV
 cache (a ring of seq_len slots): each chunk's K/V is copied into the cache
 (prefill_attn_kv_cache_update), then its queries attend to every cached key
-(prefill_attn_run_cached).  A step is the whole prompt, all chunks.
+(prefill_attn_run_cached_splitk, which splits the cached keys over several
+workgroups; --no-split runs prefill_attn_run_cached).  A step is the whole
+prompt, all chunks.
 
 --mode decode times decode attention (prefill_attn_decode): 16 sequences each
 with one new token at position 4095 against a paged bf16 KV cache of 4096
@@ -189,6 +191,8 @@ def main():
                     help="also run a plain 256 MiB elementwise copy (HBM counter calibration)")
     ap.add_argument("--mode", choices=["prefill", "chunked", "decode"], default="prefill")
     ap.add_argument("--chunk", type=int, default=1024, help="chunk length for --mode chunked")
+    ap.add_argument("--no-split", dest="split", action="store_false",
+                    help="--mode chunked without split-K over the cached keys")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -225,12 +229,15 @@ def main():
         pieces = [(torch.full((B,), p, dtype=torch.int32, device="cuda"), qd[:, p:p + n].contiguous(),
                    kd[:, p:p + n].contiguous(), vd[:, p:p + n].contiguous()) for p, n in chunks]
         outs = [torch.empty(x[1].shape, dtype=torch.float32, device="cuda") for x in pieces]
+        # Split-K over the cached keys (the library picks the split), workspace for up to 16 splits.
+        ws = torch.empty(pa.prefill_attn_run_cached_workspace_size(attn.handle, B, args.chunk, 16),
+                         dtype=torch.uint8, device="cuda")
 
         def step():
             for (off, qc, kn, vn), oc in zip(pieces, outs):
                 attn.kv_cache_update(kn, vn, kc, vc, kv_map, off, stream=stream)
                 attn.run_cached(qc, kc, vc, kv_map, pos_offsets=off, score_scale=w.score_scale, out=oc,
-                                stream=stream)
+                                stream=stream, n_split=0 if args.split else 1, workspace=ws if args.split else None)
 
     for _ in range(args.warmup):
         step()
@@ -285,7 +292,8 @@ def main():
         "dtype": "f16" if w.dtype == "bf16" else {"f32": "f32", "i16": "i8", "bf16q": "i8"}[w.dtype],
         "data": "synthetic",
         "config": {
-            "workload": w.name if args.mode == "prefill" else f"{w.name}, chunked prefill in chunks of {args.chunk}",
+            "workload": w.name if args.mode == "prefill" else
+            f"{w.name}, chunked prefill in chunks of {args.chunk}" + ("" if args.split else ", no split-K"),
             "mode": args.mode,
             "batch": w.batch,
             "seq_len": w.seq_len,

@@ -156,6 +156,26 @@ int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int batch, int 
                             float* out, float score_scale, void* stream);
 
 /*
+ * prefill_attn_run_cached_splitk: prefill_attn_run_cached with the keys of every
+ * (query block, sequence, head) split over n_split workgroups, for chunks whose
+ * prefix is long compared with the chunk (few query blocks, many keys each).
+ * Each split writes an unnormalised partial (O, running max, sum) to `workspace`
+ * (device, 16-byte aligned, caller-owned, at least
+ * prefill_attn_run_cached_workspace_size(h, batch, seq_len, n_split) bytes) and a
+ * second kernel merges them by the log-sum-exp rule (the same rule the XNet-DNN
+ * article, §三.3, uses to combine blocks of the online softmax).  n_split = 0
+ * lets the library choose; a NULL or short workspace lowers n_split to what fits,
+ * down to 1, which is prefill_attn_run_cached.  PA_IN_F32 always runs unsplit.
+ * Results equal prefill_attn_run_cached's up to the rounding of the merge.
+ */
+size_t prefill_attn_run_cached_workspace_size(const prefill_attn* h, int batch, int seq_len, int n_split);
+int prefill_attn_run_cached_splitk(const prefill_attn* h, int in_dtype, int batch, int seq_len,
+                                   const void* q, const void* k_cache, const void* v_cache, int n_slots,
+                                   const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
+                                   float* out, float score_scale, int n_split,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode attention: one new token per sequence against the KV cache.
  *
  * Sources: the page titled "手写内核实现6倍prefill加速", §3.1 (RoPE from

@@ -26,6 +26,7 @@ __all__ = [
     "prefill_attn_debug_rope_i16", "prefill_attn_debug_scores_i32", "prefill_attn_debug_scores_q16",
     "prefill_attn_kv_cache_update", "prefill_attn_run_cached", "prefill_attn_ring_map", "prefill_attn_paged_map",
     "prefill_attn_decode", "prefill_attn_decode_workspace_size",
+    "prefill_attn_run_cached_splitk", "prefill_attn_run_cached_workspace_size",
     "PrefillAttention", "EXPORTED_SYMBOLS",
 ]
 
@@ -53,6 +54,9 @@ _SIGNATURES = {
     "prefill_attn_ring_map": (_I, [_I, _I, _I, _P]),
     "prefill_attn_paged_map": (_I, [_P, _I, _I, _I, _P]),
     "prefill_attn_decode_workspace_size": (ctypes.c_size_t, [_P, _I, _I]),
+    "prefill_attn_run_cached_workspace_size": (ctypes.c_size_t, [_P, _I, _I, _I]),
+    "prefill_attn_run_cached_splitk": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _I,
+                                            _P, ctypes.c_size_t, _P]),
     "prefill_attn_decode": (_I, [_P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _I, _P,
                                  ctypes.c_size_t, _P]),
 }
@@ -233,6 +237,22 @@ def prefill_attn_paged_map(block_table, block_size, count):
     return out[:count]
 
 
+def prefill_attn_run_cached_workspace_size(handle, batch, seq_len, n_split):
+    """Bytes of workspace a split-K cached run with n_split > 1 needs (0 for n_split = 1)."""
+    return int(load_library().prefill_attn_run_cached_workspace_size(handle, batch, seq_len, n_split))
+
+
+def prefill_attn_run_cached_splitk(handle, in_dtype, batch, seq_len, q, k_cache, v_cache, n_slots, kv_map,
+                                   map_stride, pos_offsets, out, score_scale=0.0, n_split=0, workspace=None,
+                                   workspace_bytes=0, stream=None):
+    """Enqueue a split-K cached prefill pass (see the header)."""
+    _check(load_library().prefill_attn_run_cached_splitk(handle, in_dtype, batch, seq_len, _ptr(q), _ptr(k_cache),
+                                                         _ptr(v_cache), n_slots, _ptr(kv_map), map_stride,
+                                                         _ptr(pos_offsets), _ptr(out), float(score_scale), n_split,
+                                                         _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "prefill_attn_run_cached_splitk")
+
+
 def prefill_attn_decode_workspace_size(handle, batch, n_split):
     """Bytes of workspace a decode call with n_split > 1 needs (0 for n_split = 1)."""
     return int(load_library().prefill_attn_decode_workspace_size(handle, batch, n_split))
@@ -351,9 +371,11 @@ class PrefillAttention:
                                      v_cache, n_slots, stream)
 
     def run_cached(self, q, k_cache, v_cache, kv_map, pos_offsets=None, score_scale=0.0, out=None, stream=None,
-                   quantize=False):
+                   quantize=False, n_split=1, workspace=None):
         """Chunked prefill: queries q [B][S][Hq][D] at positions pos_offsets[b] + i
-        against the cached logical keys 0 .. pos_offsets[b] + i.  Returns O (float32)."""
+        against the cached logical keys 0 .. pos_offsets[b] + i.  Returns O (float32).
+        n_split != 1 (0 = chosen by the library) with a device workspace tensor splits
+        the keys over several workgroups (prefill_attn_run_cached_splitk)."""
         dt = self._dtype(q, quantize)
         B, S, Hq, D = q.shape
         if Hq != self.n_heads or D != self.head_dim or not q.is_cuda or not q.is_contiguous():
@@ -366,8 +388,13 @@ class PrefillAttention:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         elif out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
             raise ValueError("out must be contiguous float32 [B][S][n_heads][head_dim]")
-        prefill_attn_run_cached(self.handle, dt, B, S, q, k_cache, v_cache, n_slots, kv_map, stride, pos_offsets,
-                                out, score_scale, stream)
+        if workspace is None and n_split == 1:
+            prefill_attn_run_cached(self.handle, dt, B, S, q, k_cache, v_cache, n_slots, kv_map, stride,
+                                    pos_offsets, out, score_scale, stream)
+        else:
+            ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+            prefill_attn_run_cached_splitk(self.handle, dt, B, S, q, k_cache, v_cache, n_slots, kv_map, stride,
+                                           pos_offsets, out, score_scale, n_split, workspace, ws_bytes, stream)
         return out
 
     def decode(self, q, k_cache, v_cache, kv_map, pos_offsets=None, score_scale=0.0, n_split=0, workspace=None,

@@ -224,6 +224,80 @@ extern "C" int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int 
 
 namespace {
 
+size_t split_ws_bytes(const prefill_attn* h, int batch, int seq_len, int n_split) {
+    return static_cast<size_t>(batch) * seq_len * h->n_heads * n_split * (h->head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" size_t prefill_attn_run_cached_workspace_size(const prefill_attn* h, int batch, int seq_len,
+                                                         int n_split) {
+    if (!h || batch < 0 || seq_len < 0 || n_split < 1) return 0;
+    return n_split == 1 ? 0 : split_ws_bytes(h, batch, seq_len, n_split);
+}
+
+extern "C" int prefill_attn_run_cached_splitk(const prefill_attn* h, int in_dtype, int batch, int seq_len,
+                                              const void* q, const void* k_cache, const void* v_cache, int n_slots,
+                                              const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
+                                              float* out, float score_scale, int n_split, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+    if (!h || n_split < 0) return PA_EINVAL;
+    if (workspace && !aligned16(workspace)) return PA_EINVAL;
+    if (in_dtype == PA_IN_F32 || batch <= 0 || seq_len <= 0) n_split = 1;  // fp32 kernel has no split
+    if (n_split == 0) {
+        // Split only a grid that leaves CUs idle (under 256 eight-wave workgroups):
+        // aim at two rounds of them, at least four 64-key tiles per split.
+        const long long wgs256 = static_cast<long long>((seq_len + 255) / 256) * batch * h->n_heads;
+        n_split = wgs256 >= 256 ? 1 : static_cast<int>((512 + wgs256 - 1) / wgs256);
+        n_split = std::min(n_split, std::max(1, map_stride / (4 * 64)));
+    }
+    if (n_split > 1 && (!workspace || workspace_bytes < split_ws_bytes(h, batch, seq_len, 2))) n_split = 1;
+    while (n_split > 1 && split_ws_bytes(h, batch, seq_len, n_split) > workspace_bytes) --n_split;
+    if (n_split == 1)
+        return prefill_attn_run_cached(h, in_dtype, batch, seq_len, q, k_cache, v_cache, n_slots, kv_map,
+                                       map_stride, pos_offsets, out, score_scale, stream);
+
+    pa::RunArgs a;
+    int rc = prepare(h, batch, seq_len, pos_offsets, a);
+    if (rc != PA_OK) return rc;
+    const int el = elem_bytes(in_dtype);
+    if (el == 0 || !std::isfinite(score_scale)) return PA_EINVAL;
+    rc = check_cache(h, el, seq_len, n_slots, kv_map, map_stride, k_cache, v_cache);
+    if (rc != PA_OK) return rc;
+    if (!q || !out || !aligned16(q) || !aligned16(out)) return PA_EINVAL;
+    const long long grid = ((static_cast<long long>(seq_len) + 127) / 128) * batch * h->n_heads * n_split;
+    if (grid > 0x7fffffffLL) return PA_EINVAL;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.kv_map = kv_map;
+    a.map_stride = map_stride;
+    a.n_slots = n_slots;
+    a.n_split = n_split;
+    a.ws = static_cast<float*>(workspace);
+    a.score_scale = score_scale != 0.0f ? score_scale : 1.0f / std::sqrt(static_cast<float>(h->head_dim));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (in_dtype) {
+        case PA_IN_BF16: e = pa::launch_attn_bf16(h->head_dim, a, s); break;
+        case PA_IN_BF16_Q16: e = pa::launch_attn_i16q(h->head_dim, a, s); break;
+        default: e = pa::launch_attn_i16(h->head_dim, a, s); break;
+    }
+    if (e != hipSuccess) return PA_ELAUNCH;
+    pa::DecodeArgs m;
+    std::memset(&m, 0, sizeof(m));
+    m.out = out;
+    m.ws = a.ws;
+    m.batch = batch * seq_len;
+    m.n_heads = h->n_heads;
+    m.n_split = n_split;
+    e = pa::launch_split_merge(h->head_dim, m, s);
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+namespace {
+
 constexpr int kDecodeCUs = 256;
 constexpr int kDecodeMinKeysPerSplit = 256;
 

@@ -121,9 +121,8 @@ __device__ __forceinline__ float4 ld16f(const char* base, uint32_t off) {
 struct BlockPos {
     int qb, b, hq;
 };
-__device__ __forceinline__ BlockPos map_block(int n_qblocks, int batch, int n_heads) {
+__device__ __forceinline__ BlockPos map_block(int n_qblocks, int batch, int n_heads, int bid) {
     const int BH = batch * n_heads;
-    const int bid = blockIdx.x;
     int qb, bh;
     if ((BH & 7) == 0) {
         const int x = bid & 7, j = bid >> 3, hpx = BH >> 3;
@@ -145,12 +144,15 @@ __device__ __forceinline__ BlockPos map_block(int n_qblocks, int batch, int n_he
 struct Ctx {
     int b, hq, hkv, off, S, q0;
     int koff, kshift, NK;
+    int split;  // this workgroup's key range among n_split (split-K only)
 };
 
-template <int BM, bool MAPPED>
+template <int BM, bool MAPPED, bool SPLIT = false>
 __device__ __forceinline__ bool make_ctx(const RunArgs& a, Ctx& c) {
     const int n_qblocks = (a.seq_len + BM - 1) / BM;
-    const BlockPos bp = map_block(n_qblocks, a.batch, a.n_heads);
+    const int bid = SPLIT ? static_cast<int>(blockIdx.x) / a.n_split : static_cast<int>(blockIdx.x);
+    c.split = SPLIT ? static_cast<int>(blockIdx.x) % a.n_split : 0;
+    const BlockPos bp = map_block(n_qblocks, a.batch, a.n_heads, bid);
     c.b = bp.b;
     c.hq = bp.hq;
     c.hkv = bp.hq / (a.n_heads / a.n_kv_heads);
@@ -210,6 +212,29 @@ __device__ __forceinline__ Rows kv_rows(const RunArgs& a, const Ctx& c, const vo
 __device__ __forceinline__ Rows q_rows(const RunArgs& a, const Ctx& c, const void* t, int D, int el) {
     return {static_cast<const char*>(t) + q_index(a, c, 0, D) * el, static_cast<uint32_t>(a.n_heads * D * el),
             nullptr, 0, nullptr};
+}
+
+// Split-K partial results: unnormalised O of row r and split s at
+// ws[(r * n_split + s) * D], its (running max, sum) pair after all the O parts.
+__device__ __forceinline__ float* split_o(const RunArgs& a, size_t row, int split, int D) {
+    return a.ws + (row * a.n_split + split) * D;
+}
+__device__ __forceinline__ float2* split_ml(const RunArgs& a, size_t row, int split, int D) {
+    const size_t rows = static_cast<size_t>(a.batch) * a.seq_len * a.n_heads;
+    return reinterpret_cast<float2*>(a.ws + rows * a.n_split * D) + row * a.n_split + split;
+}
+
+// Split-K variant of zero_rows: empty partials (O = 0, max = -inf, sum = 0).
+template <int D, int BM, int NT>
+__device__ void zero_partials(const RunArgs& a, const Ctx& c) {
+    const int rows = min(BM, c.S - c.q0);
+    for (int idx = threadIdx.x; idx < rows * (D / 4); idx += NT) {
+        const int r = idx / (D / 4), col = idx % (D / 4);
+        const size_t row = q_index(a, c, c.q0 + r, D) / D;
+        reinterpret_cast<float4*>(split_o(a, row, c.split, D))[col] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (col == 0) *split_ml(a, row, c.split, D) = make_float2(-__builtin_huge_valf(), 0.f);
+    }
+    if (threadIdx.x == 0) atomicOr(a.status, 1);
 }
 
 // A batch element whose positions leave the tables: O = 0 and the status word is set.
@@ -842,7 +867,9 @@ struct VStage8 : VStage<D, NT> {
 // runs the softmax and the staging.  Tiles every query of the workgroup sees
 // in full run a branch-free copy of the step (no masks, no clamps).
 // MAPPED: cached prefill, keys read through the index map (see Ctx).
-template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, bool MAPPED>
+// SPLIT: the workgroup runs only its share of the key tiles and writes an
+// unnormalised partial (O, running max, sum) for a merge kernel.
+template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, bool MAPPED, bool SPLIT>
 struct FusedAttn {
     static constexpr int NT = 64 * NW;
     static constexpr int BMW = 32 * NW;
@@ -852,7 +879,7 @@ struct FusedAttn {
 
     char* lds;
     Ctx c;
-    int lq, lh, qw0, kq0, n_tiles;  // kq0: the wave's first query in key space
+    int lq, lh, qw0, kq0, n_tiles;  // kq0: the wave's first query in key space; n_tiles: end of the tile range
     typename P::KPtr kp;
     Rows vp;
     typename P::KRegs kr;
@@ -966,19 +993,33 @@ struct FusedAttn {
         lh = lane >> 5;
         qw0 = c.q0 + 32 * w;
         kq0 = c.kshift + qw0;
-        n_tiles = (c.kshift + min(c.q0 + BMW, c.S) + BN - 1) / BN;
-        const int n_full = min((c.kshift + c.q0) / BN, n_tiles);  // tiles every query of the workgroup sees whole
+        const int n_all = (c.kshift + min(c.q0 + BMW, c.S) + BN - 1) / BN;
+        const int n_full = min((c.kshift + c.q0) / BN, n_all);  // tiles every query of the workgroup sees whole
+        int t_lo = 0;
+        n_tiles = n_all;
+        if (SPLIT) {
+            const int per = (n_all + a.n_split - 1) / a.n_split;
+            t_lo = min(c.split * per, n_all);
+            n_tiles = min(t_lo + per, n_all);
+        }
         kp = P::template kptr<MAPPED>(a, c);
         vp = kv_rows<MAPPED>(a, c, a.v, D, 2);
 
-        P::template load_k<true, MAPPED>(kp, 0, kr);
-        V::template load<true, MAPPED>(vp, c.NK, 0, vr);
+        // An empty split (t_lo == n_all) loads no tile: a clamped row of a tile
+        // past the last key would be negative, and row offsets are unsigned.
+        const bool any = !SPLIT || t_lo < n_tiles;
+        if (any) {
+            P::template load_k<true, MAPPED>(kp, t_lo, kr);
+            V::template load<true, MAPPED>(vp, c.NK, t_lo, vr);
+        }
         P::load_q(a, c, qw0 + lq, logit_scale, q);
-        P::commit_k(kr, kbuf(0));
-        V::commit(vr, vbuf(0));
-        if (n_tiles > 1) {
-            P::template load_k<true, MAPPED>(kp, 1, kr);
-            P::commit_k(kr, kbuf(1));
+        if (any) {
+            P::commit_k(kr, kbuf(t_lo));
+            V::commit(vr, vbuf(t_lo));
+        }
+        if (t_lo + 1 < n_tiles) {
+            P::template load_k<true, MAPPED>(kp, t_lo + 1, kr);
+            P::commit_k(kr, kbuf(t_lo + 1));
         }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
@@ -987,14 +1028,15 @@ struct FusedAttn {
         l_b = 0.f;
         __syncthreads();
         float sa[32], sb[32];
-        qk_tile<false>(0, sa);
-        __syncthreads();  // every wave has read K'(0) before step 0 overwrites that buffer
+        if (any) qk_tile<false>(t_lo, sa);
+        __syncthreads();  // every wave has read K'(t_lo) before the first step overwrites that buffer
 
         // A steady pair loads K(t+2), K(t+3) and V(t+1), V(t+2) unclamped and runs
         // the softmax of tiles t, t+1 unmasked: every one of those tiles must lie
-        // below n_full (tile n_full itself may reach past the last key).
-        int t = 0;
-        for (; t + 3 < n_full; t += 2) {
+        // below n_full (tile n_full itself may reach past the last key) and in range.
+        int t = t_lo;
+        const int t_steady = SPLIT ? min(n_full, n_tiles) : n_full;
+        for (; t + 3 < t_steady; t += 2) {
             step<true>(t, sa, sb);
             step<true>(t + 1, sb, sa);
         }
@@ -1004,6 +1046,22 @@ struct FusedAttn {
         }
 
         if (qw0 >= c.S) return;
+        if (SPLIT) {
+            const float l = halves_sum(l_a + l_b);
+            const int qi = qw0 + lq;
+            if (qi < c.S) {
+                const size_t row = q_index(a, c, qi, D) / D;
+                float* dst = split_o(a, row, c.split, D);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<float4*>(dst + 32 * db + 8 * g + 4 * lh) =
+                            make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+                if (lh == 0) *split_ml(a, row, c.split, D) = make_float2(m_run, l);
+            }
+            return;
+        }
         const float inv = 1.0f / halves_sum(l_a + l_b);
         const int qi = qw0 + lq;
         if (qi < c.S) {
@@ -1020,14 +1078,18 @@ struct FusedAttn {
     }
 };
 
-template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, int MINB, bool MAPPED>
+template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, int MINB, bool MAPPED,
+          bool SPLIT = false>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, float logit_scale) {
-    using K = FusedAttn<D, QKT, VST, NW, MAPPED>;
+    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT>;
     __shared__ __attribute__((aligned(16))) char lds[K::kLds];
     K k;
     k.lds = lds;
-    if (!make_ctx<K::BMW, MAPPED>(a, k.c)) {
-        zero_rows<D, K::BMW, K::NT>(a, k.c);
+    if (!make_ctx<K::BMW, MAPPED, SPLIT>(a, k.c)) {
+        if (SPLIT)
+            zero_partials<D, K::BMW, K::NT>(a, k.c);
+        else
+            zero_rows<D, K::BMW, K::NT>(a, k.c);
         return;
     }
     k.run(a, logit_scale);
@@ -1262,36 +1324,47 @@ dim3 grid_for(const RunArgs& a, int bm) {
     return dim3(static_cast<unsigned>(n_qblocks) * a.batch * a.n_heads);
 }
 
-// 256-row eight-wave workgroups when they still give every CU work; otherwise
-// (short sequences, few heads) 128-row four-wave workgroups for parallelism.
-// A non-null index map selects the cached-prefill instantiation.
-template <int D, bool M>
+// Workgroup shape from prefill_uses_eight_waves; a non-null index map selects
+// the cached-prefill instantiation, n_split > 1 (with the map) the split-K one.
+template <int D, bool M, bool SP>
 void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
-    const long long wgs256 = static_cast<long long>((a.seq_len + 255) / 256) * a.batch * a.n_heads;
-    if (wgs256 >= 256) {
-        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M>), grid_for(a, 256), dim3(512), 0, s,
-                           a, a.score_scale * kLog2e);
+    const int ns = SP ? a.n_split : 1;
+    if (prefill_uses_eight_waves(a)) {
+        dim3 g = grid_for(a, 256);
+        g.x *= ns;
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP>), g, dim3(512), 0, s, a,
+                           a.score_scale * kLog2e);
     } else {
-        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16QK, VStage, 4, 2, M>), grid_for(a, 128), dim3(256), 0, s, a,
+        dim3 g = grid_for(a, 128);
+        g.x *= ns;
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16QK, VStage, 4, 2, M, SP>), g, dim3(256), 0, s, a,
                            a.score_scale * kLog2e);
     }
 }
 template <int D>
 hipError_t launch_bf16_d(const RunArgs& a, hipStream_t s) {
-    if (a.kv_map)
-        launch_bf16_dm<D, true>(a, s);
+    if (a.kv_map && a.n_split > 1)
+        launch_bf16_dm<D, true, true>(a, s);
+    else if (a.kv_map)
+        launch_bf16_dm<D, true, false>(a, s);
     else
-        launch_bf16_dm<D, false>(a, s);
+        launch_bf16_dm<D, false, false>(a, s);
     return hipGetLastError();
 }
 template <int D, template <int, int> class QKT>
 hipError_t launch_int_d(const RunArgs& a, hipStream_t s) {
-    if (a.kv_map)
+    if (a.kv_map && a.n_split > 1) {
+        dim3 g = grid_for(a, 128);
+        g.x *= a.n_split;
+        hipLaunchKernelGGL((attn_fwd_kernel<D, QKT, VStage, 4, 1, true, true>), g, dim3(256), 0, s, a,
+                           a.score_scale * kLog2e);
+    } else if (a.kv_map) {
         hipLaunchKernelGGL((attn_fwd_kernel<D, QKT, VStage, 4, 1, true>), grid_for(a, 128), dim3(256), 0, s, a,
                            a.score_scale * kLog2e);
-    else
+    } else {
         hipLaunchKernelGGL((attn_fwd_kernel<D, QKT, VStage, 4, 1, false>), grid_for(a, 128), dim3(256), 0, s, a,
                            a.score_scale * kLog2e);
+    }
     return hipGetLastError();
 }
 template <int D>
@@ -1310,6 +1383,13 @@ hipError_t launch_f32_d(const RunArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// 256-row eight-wave workgroups when they still give every CU work (counting
+// split-K copies); otherwise 128-row four-wave workgroups for parallelism.
+bool prefill_uses_eight_waves(const RunArgs& a) {
+    const long long wgs256 = static_cast<long long>((a.seq_len + 255) / 256) * a.batch * a.n_heads;
+    return wgs256 * (a.n_split > 1 ? a.n_split : 1) >= 256;
+}
 
 #define PA_DISPATCH_D(fn, d, ...)                       \
     switch (d) {                                        \

@@ -356,6 +356,19 @@ int decode_group(int n_heads, int n_kv_heads) {
     return g % 8 == 0 ? 8 : g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
 }
 
+hipError_t launch_split_merge(int head_dim, const DecodeArgs& a, hipStream_t s) {
+    const long long blocks = static_cast<long long>(a.batch) * a.n_heads;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 g(static_cast<unsigned>(blocks));
+    switch (head_dim) {
+        case 64: hipLaunchKernelGGL((decode_merge_kernel<64>), g, dim3(64), 0, s, a); break;
+        case 96: hipLaunchKernelGGL((decode_merge_kernel<96>), g, dim3(64), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((decode_merge_kernel<128>), g, dim3(64), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(int head_dim, bool f32, const DecodeArgs& a, hipStream_t s) {
     switch (head_dim) {
         case 64: return f32 ? launch_d<64, true>(a, s) : launch_d<64, false>(a, s);

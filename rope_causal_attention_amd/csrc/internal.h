@@ -28,6 +28,12 @@ struct RunArgs {
     const int32_t* kv_map;
     int map_stride;
     int n_slots;
+    // Split-K (cached prefill only): the keys of every (query block, sequence,
+    // head) are divided over n_split workgroups, each writing its unnormalised
+    // O and (max, sum) to ws: [rows][n_split][D] fp32, then [rows][n_split][2],
+    // rows = batch * seq_len * n_heads in the order of O.
+    int n_split;
+    float* ws;
 };
 
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t stream);
@@ -61,6 +67,12 @@ struct DecodeArgs {
     int n_split;
     float logit_scale;           // score_scale * log2(e)
 };
+
+// Merge of split-K partials: out[r][:] = sum_s w_s O_s / sum_s w_s l_s over the
+// rows r < a.batch * a.n_heads (DecodeArgs.batch counts row groups of n_heads).
+hipError_t launch_split_merge(int head_dim, const DecodeArgs& a, hipStream_t stream);
+// Whether a cached-prefill launch of this shape uses eight-wave workgroups.
+bool prefill_uses_eight_waves(const RunArgs& a);
 
 // Query heads served by one decode workgroup (a divisor of n_heads / n_kv_heads).
 int decode_group(int n_heads, int n_kv_heads);

@@ -338,3 +338,102 @@ def test_cache_calls_reject_bad_arguments():
         assert attn.status() == pa.PA_OK
     finally:
         attn.close()
+
+
+# ------------------------------------------------------------ split-K cached prefill
+
+# Split and unsplit runs round P~ to fp16 against different running maxima:
+# each element may differ by two half-ulps, 2^-10 relative, times |V| up to
+# ~4 in these workloads (per-head scales up to 2, 2 sigma) -> 4e-3 max-abs.
+# Far below the oracle bars, which both runs must meet on their own.
+SPLIT_TOL_MAX = 4e-3
+SPLIT_TOL_MEAN = 1e-4  # a key dropped from a 2000-key row moves O by ~5e-4 on average
+
+SPLIT_CASES = [
+    # name, B, Hq, Hkv, D, dtype, theta, prefix, S, layout, n_slots, n_split
+    ("sk_bf16_d128_paged", 2, 8, 2, 128, "bf16", 1e4, [700, 1300], 150, "paged", 4096, 4),
+    ("sk_bf16_d96_ring_auto", 1, 4, 4, 96, "bf16", 1e4, [2000], 100, "ring", 4096, 0),
+    ("sk_bf16_d64_many", 2, 4, 2, 64, "bf16", 1e4, [64, 5], 77, "paged", 1024, 9),
+    ("sk_i16_d128", 1, 4, 2, 128, "i16", 1e4, [900], 128, "paged", 2048, 3),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_k_cached_prefill(case):
+    """Split-K partials merged by the log-sum-exp rule: against the oracle at the
+    usual bars, and against the unsplit cached run (they differ only through the
+    fp16 rounding of P~ relative to each split's running max)."""
+    *head, n_split = case
+    c = Case(*head)
+    announce(c.name, "n_split", n_split)
+    attn = _handle(c)
+    try:
+        off = torch.tensor(c.prefix, dtype=torch.int32, device="cuda")
+        qd, kcd, vcd, mapd = c.q.cuda(), c.kc.cuda(), c.vc.cuda(), torch.from_numpy(c.map).cuda()
+        ws = torch.empty(pa.prefill_attn_run_cached_workspace_size(attn.handle, c.B, c.S, 16), dtype=torch.uint8,
+                         device="cuda")
+        o_split = attn.run_cached(qd, kcd, vcd, mapd, pos_offsets=off, score_scale=c.scale, n_split=n_split,
+                                  workspace=ws)
+        o_one = attn.run_cached(qd, kcd, vcd, mapd, pos_offsets=off, score_scale=c.scale)
+        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
+        o_split, o_one = o_split.cpu(), o_one.cpu()
+    finally:
+        attn.close()
+    mx, mean = errors(o_split.numpy(), o_one.numpy())
+    assert mx <= SPLIT_TOL_MAX and mean <= SPLIT_TOL_MEAN, f"split vs unsplit {mx:.3e} / {mean:.3e}"
+    mx, mean = assert_close(o_split.numpy(), c.oracle(), "bf16")
+    announce(c.name, f"max {mx:.2e} mean {mean:.2e}")
+
+
+def test_split_k_long_prompt_chunks():
+    """The 1 x 32 x 4096 x 96 long prompt in chunks of 1024 with split-K against
+    the one-shot prefill (merge rounding only) and the oracle on sampled rows."""
+    w = synth.WORKLOADS["mha_bf16_h32_s4096_d96"]
+    announce(w.name, "chunks of 1024, split-K")
+    q, k, v = synth.make_inputs(w)
+    kv_map = torch.from_numpy(oracle.ring_index_map(4096, 1000, 4096).astype(np.int32)[None, :]).cuda()
+    attn = pa.PrefillAttention(w.n_heads, w.n_kv_heads, w.head_dim, w.seq_len, w.rope_theta)
+    try:
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        kc = torch.zeros((4096, 32, 96), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        ws = torch.empty(pa.prefill_attn_run_cached_workspace_size(attn.handle, 1, 1024, 8), dtype=torch.uint8,
+                         device="cuda")
+        outs = []
+        for p in range(0, 4096, 1024):
+            off = torch.tensor([p], dtype=torch.int32, device="cuda")
+            attn.kv_cache_update(kd[:, p:p + 1024].contiguous(), vd[:, p:p + 1024].contiguous(), kc, vc, kv_map, off)
+            outs.append(attn.run_cached(qd[:, p:p + 1024].contiguous(), kc, vc, kv_map, pos_offsets=off, n_split=0,
+                                        workspace=ws))
+        o_chunk = torch.cat(outs, dim=1).cpu()
+        o_plain = attn(qd, kd, vd).cpu()
+        assert attn.status() == pa.PA_OK
+    finally:
+        attn.close()
+    mx, mean = errors(o_chunk.numpy(), o_plain.numpy())
+    assert mx <= SPLIT_TOL_MAX and mean <= SPLIT_TOL_MEAN, (mx, mean)
+    from gpu_common import oracle_rows, sample_rows
+    rows = sample_rows(w, 48, seed=12)
+    got = np.stack([o_chunk[b, i, h].numpy() for b, h, i in rows])
+    mx, _ = errors(got, oracle_rows(w, q, k, v, rows))
+    assert mx <= 1e-2, mx
+
+
+def test_split_k_range_error_gives_zeros():
+    c = Case("sk_range", 2, 2, 1, 64, "bf16", 1e4, [10, 20], 40, "paged", 512)
+    announce(c.name)
+    attn = _handle(c, max_seq=256)
+    try:
+        off = torch.tensor([10, 30], dtype=torch.int32, device="cuda")  # 30 + 40 > map_stride 60
+        out = torch.full(c.q.shape, 7.0, dtype=torch.float32, device="cuda")
+        ws = torch.empty(pa.prefill_attn_run_cached_workspace_size(attn.handle, 2, 40, 4), dtype=torch.uint8,
+                         device="cuda")
+        attn.run_cached(c.q.cuda(), c.kc.cuda(), c.vc.cuda(), torch.from_numpy(c.map).cuda(), pos_offsets=off,
+                        out=out, n_split=4, workspace=ws)
+        assert attn.status() == pa.PA_ERANGE
+        o = out.cpu()
+        assert torch.all(o[1] == 0)
+        assert torch.all(torch.isfinite(o[0])) and not torch.all(o[0] == 7.0)
+    finally:
+        attn.close()
