@@ -24,13 +24,17 @@ Pages cited (by title and section):
   physical slot (``kv_cache.py``).
 * the 2kiu.com retelling, §3.3, and the MNN-on-K3 blog, §四, for the
   per-token dynamic int16 quantisation of float Q/K (``quantize.py``).
+* the 2kiu.com retelling, §3.3, for the fixed-point softmax: exp as 16
+  straight-line segments on [-8, 8] and a division-free reciprocal
+  (``pwl_softmax.py``).
 
 The blocked online softmax of those pages reaches, in exact arithmetic, the
 plain causal softmax-attention result; so this oracle is that plain
 definition: explicit RoPE, the full causal score matrix, a two-pass softmax.
 
 Parity pins (tests/test_oracle_pins.py, tests/test_oracle_cache_pins.py,
-tests/test_oracle_quant_pins.py) cover every function here; none is
+tests/test_oracle_quant_pins.py, tests/test_oracle_pwl_pins.py) cover every
+function here; none is
 "parity unpinned".  Two *inputs* are readings rather than derivations and are
 documented as such with the workloads: the int16 ``score_scale`` and the
 per-head scale recipe of the long-prompt workload.
@@ -57,6 +61,12 @@ from .quantize import (
     quantize_rows_i16,
     attention_i16_quantized,
     attention_i16_quantized_rows,
+)
+from .pwl_softmax import (
+    pwl_exp,
+    newton_reciprocal,
+    pwl_softmax_rows,
+    attention_i16_pwl,
 )
 from .fixed_point import (
     rope_table_q14,
@@ -88,4 +98,8 @@ __all__ = [
     "quantize_rows_i16",
     "attention_i16_quantized",
     "attention_i16_quantized_rows",
+    "pwl_exp",
+    "newton_reciprocal",
+    "pwl_softmax_rows",
+    "attention_i16_pwl",
 ]
