@@ -191,6 +191,8 @@ def main():
                     help="also run a plain 256 MiB elementwise copy (HBM counter calibration)")
     ap.add_argument("--mode", choices=["prefill", "chunked", "decode"], default="prefill")
     ap.add_argument("--chunk", type=int, default=1024, help="chunk length for --mode chunked")
+    ap.add_argument("--pwl-softmax", action="store_true",
+                    help="int16 workload with the piecewise-linear softmax (PA_IN_I16_PWL)")
     ap.add_argument("--no-split", dest="split", action="store_false",
                     help="--mode chunked without split-K over the cached keys")
     args = ap.parse_args()
@@ -217,7 +219,8 @@ def main():
 
     if args.mode == "prefill":
         def step():
-            attn(qd, kd, vd, score_scale=w.score_scale, out=out, stream=stream, quantize=w.dtype == "bf16q")
+            attn(qd, kd, vd, score_scale=w.score_scale, out=out, stream=stream, quantize=w.dtype == "bf16q",
+                 pwl_softmax=args.pwl_softmax)
     else:
         # Ring cache of seq_len slots starting at slot 1000 (wraps), one map row per sequence.
         S, B = w.seq_len, w.batch
@@ -295,6 +298,7 @@ def main():
             "workload": w.name if args.mode == "prefill" else
             f"{w.name}, chunked prefill in chunks of {args.chunk}" + ("" if args.split else ", no split-K"),
             "mode": args.mode,
+            "softmax": "piecewise-linear" if args.pwl_softmax else "exp",
             "batch": w.batch,
             "seq_len": w.seq_len,
             "n_heads": w.n_heads,

@@ -56,10 +56,15 @@ enum prefill_attn_dtype {
     PA_IN_F32 = 0,  /* Q, K, V float32; products on the fp32 matrix cores */
     PA_IN_BF16 = 1, /* Q, K, V bfloat16; rotated Q'/K', P and V rounded to fp16 for the matrix cores, fp32 accumulate */
     PA_IN_I16 = 2,  /* Q, K int16 fixed point, V bfloat16; integer RoPE, exact int32 scores, fp32 softmax */
-    PA_IN_BF16_Q16 = 3 /* Q, K, V bfloat16; each (token, head) row of Q and K quantised inside the kernel to
+    PA_IN_BF16_Q16 = 3, /* Q, K, V bfloat16; each (token, head) row of Q and K quantised inside the kernel to
                           int16 codes, round-half-even(x * 2047 / max|x|) in fp32 (the 2kiu.com retelling, §3.3:
                           per-token dynamic activation scale), then the PA_IN_I16 path with
                           logit = (int32 score) * score_scale * (max|q| / 2047) * (max|k| / 2047) */
+    PA_IN_I16_PWL = 4  /* as PA_IN_I16, with the softmax of the 2kiu.com retelling, §3.3: exp of
+                          x = logit - (row max) as the chord of e^x between the integer knots floor(x) and
+                          floor(x) + 1 (16 unit segments on [-8, 8)), 0 below -8, and the normalisation by
+                          a Newton-Raphson reciprocal (seed 48/17 - 32/17 f, three steps); the row max comes
+                          from a first pass over the keys.  prefill_attn_run only. */
 };
 
 enum prefill_attn_status {

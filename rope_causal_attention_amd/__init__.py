@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "PA_IN_F32", "PA_IN_BF16", "PA_IN_I16", "PA_IN_BF16_Q16",
+    "PA_IN_F32", "PA_IN_BF16", "PA_IN_I16", "PA_IN_BF16_Q16", "PA_IN_I16_PWL",
     "PA_OK", "PA_EINVAL", "PA_ENOMEM", "PA_EDEVICE", "PA_ELAUNCH", "PA_ERANGE",
     "PrefillAttnError", "load_library", "library_path",
     "prefill_attn_init", "prefill_attn_run", "prefill_attn_status", "prefill_attn_destroy",
@@ -30,7 +30,7 @@ __all__ = [
     "PrefillAttention", "EXPORTED_SYMBOLS",
 ]
 
-PA_IN_F32, PA_IN_BF16, PA_IN_I16, PA_IN_BF16_Q16 = 0, 1, 2, 3
+PA_IN_F32, PA_IN_BF16, PA_IN_I16, PA_IN_BF16_Q16, PA_IN_I16_PWL = 0, 1, 2, 3, 4
 PA_OK, PA_EINVAL, PA_ENOMEM, PA_EDEVICE, PA_ELAUNCH, PA_ERANGE = 0, -1, -2, -3, -4, -5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -326,10 +326,16 @@ class PrefillAttention:
             raise ValueError("pos_offsets must be a device int32 tensor with one entry per batch element")
         return dt, B, S
 
-    def __call__(self, q, k, v, pos_offsets=None, score_scale=0.0, out=None, stream=None, quantize=False):
+    def __call__(self, q, k, v, pos_offsets=None, score_scale=0.0, out=None, stream=None, quantize=False,
+                 pwl_softmax=False):
         """O (float32) of q [B][S][Hq][D], k/v [B][S][Hkv][D].  quantize=True runs bfloat16
-        inputs through the in-kernel per-token int16 quantisation (PA_IN_BF16_Q16)."""
+        inputs through the in-kernel per-token int16 quantisation (PA_IN_BF16_Q16);
+        pwl_softmax=True runs int16 inputs with the piecewise-linear softmax (PA_IN_I16_PWL)."""
         dt, B, S = self._validate(q, k, v, pos_offsets, out, quantize)
+        if pwl_softmax:
+            if dt != PA_IN_I16:
+                raise TypeError("pwl_softmax=True takes int16 q/k")
+            dt = PA_IN_I16_PWL
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         prefill_attn_run(self.handle, dt, B, S, q, k, v, pos_offsets, out, score_scale, stream)

@@ -120,7 +120,8 @@ extern "C" int prefill_attn_run(const prefill_attn* h, int in_dtype, int batch, 
     pa::RunArgs a;
     const int rc = prepare(h, batch, seq_len, pos_offsets, a);
     if (rc != PA_OK) return rc;
-    if (in_dtype != PA_IN_F32 && in_dtype != PA_IN_BF16 && in_dtype != PA_IN_I16 && in_dtype != PA_IN_BF16_Q16)
+    if (in_dtype != PA_IN_F32 && in_dtype != PA_IN_BF16 && in_dtype != PA_IN_I16 && in_dtype != PA_IN_BF16_Q16 &&
+        in_dtype != PA_IN_I16_PWL)
         return PA_EINVAL;
     if (!std::isfinite(score_scale)) return PA_EINVAL;
     if (batch == 0 || seq_len == 0) return PA_OK;
@@ -137,6 +138,7 @@ extern "C" int prefill_attn_run(const prefill_attn* h, int in_dtype, int batch, 
         case PA_IN_F32: e = pa::launch_attn_f32(h->head_dim, a, s); break;
         case PA_IN_BF16: e = pa::launch_attn_bf16(h->head_dim, a, s); break;
         case PA_IN_BF16_Q16: e = pa::launch_attn_i16q(h->head_dim, a, s); break;
+        case PA_IN_I16_PWL: e = pa::launch_attn_i16pwl(h->head_dim, a, s); break;
         default: e = pa::launch_attn_i16(h->head_dim, a, s); break;
     }
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;

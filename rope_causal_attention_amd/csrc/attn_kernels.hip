@@ -591,6 +591,17 @@ struct I16QK {
     }
 };
 
+// 1/l without a divide: l = f 2^e with f in [0.5, 1), Newton-Raphson from the
+// linear seed 48/17 - 32/17 f (error at most 1/17), three steps, then 2^-e.
+__device__ __forceinline__ float newton_reciprocal(float l) {
+    const float f = __builtin_amdgcn_frexp_mantf(l);
+    const int e = __builtin_amdgcn_frexp_expf(l);
+    float r = fmaf(-32.0f / 17.0f, f, 48.0f / 17.0f);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) r = r * fmaf(-f, r, 2.0f);
+    return __builtin_amdgcn_ldexpf(r, -e);
+}
+
 // ------------------------------------------------ Q.K^T policy: bf16 inputs quantised in-kernel
 
 // Per-token dynamic int16 quantisation (the 2kiu.com retelling, §3.3): each
@@ -869,7 +880,11 @@ struct VStage8 : VStage<D, NT> {
 // MAPPED: cached prefill, keys read through the index map (see Ctx).
 // SPLIT: the workgroup runs only its share of the key tiles and writes an
 // unnormalised partial (O, running max, sum) for a merge kernel.
-template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, bool MAPPED, bool SPLIT>
+// PWL: the piecewise-linear softmax (see softmax_pwl): a first pass over the
+// key tiles finds each row's maximum logit, the main loop then weights every
+// key by the chord approximation of exp relative to that maximum.
+template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, bool MAPPED, bool SPLIT,
+          bool PWL = false>
 struct FusedAttn {
     static constexpr int NT = 64 * NW;
     static constexpr int BMW = 32 * NW;
@@ -878,6 +893,7 @@ struct FusedAttn {
     static constexpr int kLds = 2 * P::kBytes + 2 * V::kBytes;
 
     char* lds;
+    const float* knots;  // PWL only: e^-n, n = 0..8
     Ctx c;
     int lq, lh, qw0, kq0, n_tiles;  // kq0: the wave's first query in key space; n_tiles: end of the tile range
     typename P::KPtr kp;
@@ -956,6 +972,61 @@ struct FusedAttn {
             }
     }
 
+    // exp(x) for x = logit - row max <= 0 as the chord of e^x between the
+    // integer knots floor(x) and floor(x) + 1 (16 unit segments on [-8, 8) in
+    // the 2kiu.com retelling, §3.3; only [-8, 0] occurs here), 0 below -8.
+    // knots[n] = e^-n, n = 0..8, staged in LDS.
+    __device__ __forceinline__ float pwl_exp(float x) const {
+        if (!(x >= -8.0f)) return 0.0f;
+        const float k = __builtin_floorf(x);
+        const float ek = knots[min(static_cast<int>(-k), 8)];
+        return ek * fmaf(1.71828182845904524f, x - k, 1.0f);
+    }
+
+    // Masked maximum of the visible logits of tile t for this lane's query.
+    __device__ __forceinline__ float tile_max(int t, int na, float* s) const {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int k0 = t * BN + 32 * kb;
+            if (kb < na) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const bool vis = k0 + acc_row(v, lh) <= kq0 + lq;
+                    mx = fmaxf(mx, vis ? s[16 * kb + v] : kNegInf);
+                }
+            }
+        }
+        return mx;
+    }
+
+    // Weights of tile t against the fixed row maximum m_run (no rescale).
+    template <bool FULL>
+    __device__ __forceinline__ void softmax_pwl(int t, int na, float* s, uint32_t* pk) {
+        const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb < na) {
+                const int k0 = t * BN + 32 * kb;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    float w[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int v = 2 * j + e;
+                        const bool vis = FULL || k0 + acc_row(v, lh) <= kq0 + lq;
+                        w[e] = vis ? pwl_exp(s[16 * kb + v] - m_run) : 0.0f;
+                    }
+                    const uint32_t p = pack_h2(w[0], w[1]);
+                    pk[8 * kb + j] = p;
+                    if (j & 1)
+                        l_b = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), ones, l_b, false);
+                    else
+                        l_a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), ones, l_a, false);
+                }
+            }
+    }
+
     __device__ __forceinline__ void pv_tile(int t, int na, const uint32_t* pk) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -978,7 +1049,12 @@ struct FusedAttn {
         if (ld_v) V::template load<!STEADY, MAPPED>(vp, c.NK, t + 1, vr);
         const int na = STEADY ? 2 : nact(t);
         uint32_t pk[16];
-        if (na > 0) softmax<STEADY>(t, na, s, pk);
+        if (na > 0) {
+            if (PWL)
+                softmax_pwl<STEADY>(t, na, s, pk);
+            else
+                softmax<STEADY>(t, na, s, pk);
+        }
         if (ld_v) qk_tile<STEADY>(t + 1, sn);
         if (na > 0) pv_tile(t, na, pk);
         if (ld_k) P::commit_k(kr, kbuf(t));
@@ -1005,6 +1081,25 @@ struct FusedAttn {
         kp = P::template kptr<MAPPED>(a, c);
         vp = kv_rows<MAPPED>(a, c, a.v, D, 2);
 
+        float pwl_max = kNegInf;
+        if (PWL) {
+            // First pass: the maximum visible logit of every query row.
+            P::load_q(a, c, qw0 + lq, logit_scale, q);
+            for (int t = 0; t < n_tiles; ++t) {
+                P::template load_k<true, MAPPED>(kp, t, kr);
+                __syncthreads();  // the previous tile's reads are done
+                P::commit_k(kr, kbuf(0));
+                __syncthreads();
+                const int na = nact(t);
+                float s1[32];
+                if (na >= 1) P::qk(kbuf(0), 0, q, s1, lq, lh);
+                if (na == 2) P::qk(kbuf(0), 1, q, s1 + 16, lq, lh);
+                if (na > 0) pwl_max = fmaxf(pwl_max, tile_max(t, na, s1));
+            }
+            pwl_max = halves_max(pwl_max);
+            __syncthreads();  // buffer 0 is restaged below
+        }
+
         // An empty split (t_lo == n_all) loads no tile: a clamped row of a tile
         // past the last key would be negative, and row offsets are unsigned.
         const bool any = !SPLIT || t_lo < n_tiles;
@@ -1023,7 +1118,7 @@ struct FusedAttn {
         }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-        m_run = kNegInf;
+        m_run = PWL ? pwl_max : kNegInf;
         l_a = 0.f;
         l_b = 0.f;
         __syncthreads();
@@ -1062,7 +1157,7 @@ struct FusedAttn {
             }
             return;
         }
-        const float inv = 1.0f / halves_sum(l_a + l_b);
+        const float inv = PWL ? newton_reciprocal(halves_sum(l_a + l_b)) : 1.0f / halves_sum(l_a + l_b);
         const int qi = qw0 + lq;
         if (qi < c.S) {
             float* orow = a.out + q_index(a, c, qi, D);
@@ -1079,12 +1174,21 @@ struct FusedAttn {
 };
 
 template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, int MINB, bool MAPPED,
-          bool SPLIT = false>
+          bool SPLIT = false, bool PWL = false>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, float logit_scale) {
-    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT>;
+    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT, PWL>;
     __shared__ __attribute__((aligned(16))) char lds[K::kLds];
+    __shared__ float knots[PWL ? 9 : 1];
     K k;
     k.lds = lds;
+    k.knots = knots;
+    if (PWL && threadIdx.x < 9) {
+        // e^-n, n = 0..8
+        constexpr float kE[9] = {1.0f, 0.36787944117144233f, 0.1353352832366127f, 0.049787068367863944f,
+                                 0.01831563888873418f, 0.006737946999085467f, 0.0024787521766663585f,
+                                 0.0009118819655545162f, 0.00033546262790251185f};
+        knots[threadIdx.x] = kE[threadIdx.x];
+    }
     if (!make_ctx<K::BMW, MAPPED, SPLIT>(a, k.c)) {
         if (SPLIT)
             zero_partials<D, K::BMW, K::NT>(a, k.c);
@@ -1371,6 +1475,13 @@ template <int D>
 hipError_t launch_i16_d(const RunArgs& a, hipStream_t s) { return launch_int_d<D, I16QK>(a, s); }
 template <int D>
 hipError_t launch_i16q_d(const RunArgs& a, hipStream_t s) { return launch_int_d<D, I16QuantQK>(a, s); }
+// Piecewise-linear softmax: logits in natural units (no log2 e factor).
+template <int D>
+hipError_t launch_i16pwl_d(const RunArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, I16QK, VStage, 4, 1, false, false, true>), grid_for(a, 128), dim3(256), 0,
+                       s, a, a.score_scale);
+    return hipGetLastError();
+}
 template <int D>
 hipError_t launch_f32_d(const RunArgs& a, hipStream_t s) {
     if (a.kv_map)
@@ -1402,6 +1513,9 @@ bool prefill_uses_eight_waves(const RunArgs& a) {
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_bf16_d, head_dim, a, s) }
 hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_i16_d, head_dim, a, s) }
 hipError_t launch_attn_i16q(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_i16q_d, head_dim, a, s) }
+hipError_t launch_attn_i16pwl(int head_dim, const RunArgs& a, hipStream_t s) {
+    PA_DISPATCH_D(launch_i16pwl_d, head_dim, a, s)
+}
 hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t s) { PA_DISPATCH_D(launch_f32_d, head_dim, a, s) }
 
 hipError_t launch_kv_cache_update(int head_dim, int el, const RunArgs& a, void* dst_k, void* dst_v, hipStream_t s) {

@@ -41,6 +41,8 @@ hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t stream);
 hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t stream);
 // bf16 Q/K quantised in-kernel per (token, head) row to int16, then the int16 path.
 hipError_t launch_attn_i16q(int head_dim, const RunArgs& a, hipStream_t stream);
+// int16 Q/K with the piecewise-linear softmax and Newton reciprocal (two passes).
+hipError_t launch_attn_i16pwl(int head_dim, const RunArgs& a, hipStream_t stream);
 
 // Copies the new tokens' K/V ([batch][seq_len][n_kv_heads][D], `el` bytes per
 // element) into their cache slots; a.k/a.v are the new K/V, dst_k/dst_v the caches.

@@ -308,3 +308,56 @@ def test_quantised_cached_equals_quantised_prefill_bitwise():
         assert torch.equal(o_plain, o_cached)
     finally:
         attn.close()
+
+
+# ------------------------------------------------------------ int16 with the piecewise-linear softmax
+
+PWL_SMALL = [
+    # name, B, Hq, Hkv, S, D, offsets, score scale
+    ("pwl_d128_gqa_ragged", 2, 4, 2, 300, 128, [0, 17], 2.0 ** -22 / 11.3137085),
+    ("pwl_d96", 1, 2, 2, 257, 96, None, 2.0 ** -22 / 9.797959),
+    ("pwl_d64_sharp", 1, 2, 1, 130, 64, None, 2.0 ** -16),  # logits spread far past the -8 cut-off
+]
+
+
+def _pwl_oracle(w, q, k, v, offs):
+    return oracle.attention_i16_pwl(q.numpy(), k.numpy(), synth.to_f64(v), pos_offsets=offs,
+                                    rope_theta=w.rope_theta, score_scale=w.score_scale)
+
+
+def _pwl_gpu(w, q, k, v, offs=None, max_seq=None):
+    attn = pa.PrefillAttention(w.n_heads, w.n_kv_heads, w.head_dim, max_seq or w.seq_len, w.rope_theta)
+    try:
+        qd, kd, vd = to_dev(q, k, v)
+        od = None if offs is None else torch.tensor(offs, dtype=torch.int32, device="cuda")
+        o = attn(qd, kd, vd, pos_offsets=od, score_scale=w.score_scale, pwl_softmax=True)
+        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
+        return o.cpu().numpy()
+    finally:
+        attn.close()
+
+
+@pytest.mark.parametrize("case", PWL_SMALL, ids=[c[0] for c in PWL_SMALL])
+def test_pwl_softmax_small_full_compare(case):
+    """Against the oracle's piecewise-linear softmax (same definition); the
+    bar is the bf16 one, the weights being rounded to fp16 for P.V."""
+    name, B, Hq, Hkv, S, D, offs, scale = case
+    announce(name)
+    max_seq = S + (max(offs) if offs else 0)
+    w = synth.Workload(name, B, Hq, Hkv, S, D, "i16", 1e4, sum(map(ord, name)), score_scale=scale)
+    q, k, v = synth.make_inputs(w)
+    got = _pwl_gpu(w, q, k, v, offs, max_seq)
+    mx, mean = assert_close(got, _pwl_oracle(w, q, k, v, offs), "bf16")
+    announce(name, f"max {mx:.2e} mean {mean:.2e}")
+
+
+def test_pwl_softmax_int16_workload():
+    w = synth.WORKLOADS["i16_h32_s2048_d128"]
+    announce(w.name, "pwl softmax")
+    q, k, v = synth.make_inputs(w)
+    got = _pwl_gpu(w, q, k, v)
+    for h in (0, 13, 31):
+        one = synth.workload(w.name, n_heads=1, n_kv_heads=1)
+        want = _pwl_oracle(one, q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1], None)
+        assert_close(got[:, :, h:h + 1], want, "bf16")
