@@ -883,19 +883,22 @@ struct VStage8 : VStage<D, NT> {
 // PWL: the piecewise-linear softmax (see softmax_pwl): a first pass over the
 // key tiles finds each row's maximum logit, the main loop then weights every
 // key by the chord approximation of exp relative to that maximum.
+// PP: the two-group schedule of run_pp (eight waves, three LDS buffers).
 template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, bool MAPPED, bool SPLIT,
-          bool PWL = false>
+          bool PWL = false, bool PP = false>
 struct FusedAttn {
     static constexpr int NT = 64 * NW;
     static constexpr int BMW = 32 * NW;
     using P = QKT<D, NT>;
     using V = VST<D, NT>;
-    static constexpr int kLds = 2 * P::kBytes + 2 * V::kBytes;
+    static_assert(!PP || (NW == 8 && !PWL), "the two-group schedule needs eight waves");
+    static constexpr int kBufs = PP ? 3 : 2;
+    static constexpr int kLds = kBufs * (P::kBytes + V::kBytes);
 
     char* lds;
     const float* knots;  // PWL only: e^-n, n = 0..8
     Ctx c;
-    int lq, lh, qw0, kq0, n_tiles;  // kq0: the wave's first query in key space; n_tiles: end of the tile range
+    int lq, lh, qw0, kq0, t_lo, n_tiles;  // kq0: the wave's first query in key space; [t_lo, n_tiles): tile range
     typename P::KPtr kp;
     Rows vp;
     typename P::KRegs kr;
@@ -904,9 +907,10 @@ struct FusedAttn {
     f32x16 o[D / 32];
     float m_run, l_a, l_b;
 
-    __device__ __forceinline__ char* kbuf(int t) const { return lds + (t & 1) * P::kBytes; }
+    __device__ __forceinline__ int slot(int t) const { return PP ? (t - t_lo) % 3 : (t & 1); }
+    __device__ __forceinline__ char* kbuf(int t) const { return lds + slot(t) * P::kBytes; }
     __device__ __forceinline__ _Float16* vbuf(int t) const {
-        return reinterpret_cast<_Float16*>(lds + 2 * P::kBytes + (t & 1) * V::kBytes);
+        return reinterpret_cast<_Float16*>(lds + kBufs * P::kBytes + slot(t) * V::kBytes);
     }
     // Active 32-key blocks of tile t for this wave (a prefix of {0, 1}); wave-uniform.
     __device__ __forceinline__ int nact(int t) const {
@@ -938,15 +942,21 @@ struct FusedAttn {
                 }
             }
         }
-        float mx = kNegInf;
+        // Row maximum; the two-group schedule reduces it as four independent
+        // chains and forms the probabilities against the current running max
+        // while the maximum is still being reduced, so only a step whose
+        // maximum moves the running max (rare) forms them again.
+        float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             if (kb < na) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[16 * kb + v]);
+                for (int v = 0; v < 16; ++v) m4[PP ? (v & 3) : 0] = fmaxf(m4[PP ? (v & 3) : 0], s[16 * kb + v]);
             }
-        mx = halves_max(mx);
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
+        if (PP) exp_tile(na, s, pk);
+        const float mx = halves_max(PP ? fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) : m4[0]);
+        const bool moved = __builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0;
+        if (moved) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = fast_exp2(m_run - m_new);
             m_run = m_new;
@@ -955,20 +965,34 @@ struct FusedAttn {
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
         }
+        if (PP && moved) exp_tile(na, s, pk);
         const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             if (kb < na) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const uint32_t p = pack_h2(fast_exp2(s[16 * kb + 2 * j] - m_run),
-                                               fast_exp2(s[16 * kb + 2 * j + 1] - m_run));
-                    pk[8 * kb + j] = p;
+                    if (!PP)
+                        pk[8 * kb + j] = pack_h2(fast_exp2(s[16 * kb + 2 * j] - m_run),
+                                                 fast_exp2(s[16 * kb + 2 * j + 1] - m_run));
+                    const f16x2 p = __builtin_bit_cast(f16x2, pk[8 * kb + j]);
                     if (j & 1)
-                        l_b = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), ones, l_b, false);
+                        l_b = __builtin_amdgcn_fdot2(p, ones, l_b, false);
                     else
-                        l_a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), ones, l_a, false);
+                        l_a = __builtin_amdgcn_fdot2(p, ones, l_a, false);
                 }
+            }
+    }
+
+    // P~ = exp2(S - m_run) as packed f16 pairs.
+    __device__ __forceinline__ void exp_tile(int na, const float* s, uint32_t* pk) const {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb < na) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    pk[8 * kb + j] = pack_h2(fast_exp2(s[16 * kb + 2 * j] - m_run),
+                                             fast_exp2(s[16 * kb + 2 * j + 1] - m_run));
             }
     }
 
@@ -1062,6 +1086,151 @@ struct FusedAttn {
         __syncthreads();
     }
 
+    // Two-group schedule (eight waves).  Each tile t is split into two phases
+    // separated by workgroup barriers:
+    //   vector phase t: commit K(t+2) -> K' and V(t+1) -> V^T (registers loaded
+    //                   two phases earlier), issue the global loads of K(t+3)
+    //                   and V(t+2), softmax of S(t) -> P~(t)     (VALU, exp2)
+    //   matrix phase t: O^T += V^T(t) P~(t)^T, S(t+1) = K'(t+1) Q'^T  (MFMA)
+    // Waves 4-7 pass one extra barrier before the loop and waves 0-3 one after
+    // it, so the second group runs one phase behind the first: on each SIMD one
+    // wave feeds the matrix cores while the other keeps the vector unit busy,
+    // and S needs one register buffer instead of two.  Three LDS buffers for K'
+    // and V^T keep every tile whole from the end of the phase that completes it
+    // until the lagging group has read it.
+    // A workgroup barrier that the compiler may not move any instruction
+    // across, so each phase keeps its own work.
+    __device__ __forceinline__ static void phase_barrier() {
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    template <bool STEADY>
+    __device__ __forceinline__ int vector_phase(int t, float* s, uint32_t* pk) {
+        if (STEADY || t + 2 < n_tiles) P::commit_k(kr, kbuf(t + 2));
+        if (STEADY || t + 1 < n_tiles) V::commit(vr, vbuf(t + 1));
+        if (STEADY || t + 3 < n_tiles) P::template load_k<!STEADY, MAPPED>(kp, t + 3, kr);
+        if (STEADY || t + 2 < n_tiles) V::template load<!STEADY, MAPPED>(vp, c.NK, t + 2, vr);
+        const int na = STEADY ? 2 : nact(t);
+        if (na > 0) softmax<STEADY>(t, na, s, pk);
+        return na;
+    }
+    template <bool STEADY>
+    __device__ __forceinline__ void matrix_phase(int t, int na, const uint32_t* pk, float* s) {
+        if (na > 0) pv_tile(t, na, pk);
+        if (STEADY || t + 1 < n_tiles) qk_tile<STEADY>(t + 1, s);
+    }
+
+    __device__ __forceinline__ void run_pp(const RunArgs& a, float logit_scale) {
+        const int lane = threadIdx.x & 63;
+        const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+        lq = lane & 31;
+        lh = lane >> 5;
+        qw0 = c.q0 + 32 * w;
+        kq0 = c.kshift + qw0;
+        const int n_all = (c.kshift + min(c.q0 + BMW, c.S) + BN - 1) / BN;
+        const int n_full = min((c.kshift + c.q0) / BN, n_all);
+        t_lo = 0;
+        n_tiles = n_all;
+        if (SPLIT) {
+            const int per = (n_all + a.n_split - 1) / a.n_split;
+            t_lo = min(c.split * per, n_all);
+            n_tiles = min(t_lo + per, n_all);
+        }
+        kp = P::template kptr<MAPPED>(a, c);
+        vp = kv_rows<MAPPED>(a, c, a.v, D, 2);
+
+        // Prologue: K'(t_lo), K'(t_lo+1) and V^T(t_lo) in LDS; K(t_lo+2) and
+        // V(t_lo+1) in registers for the first vector phase.  An empty split
+        // loads nothing (a clamped row past the last key would be negative).
+        const bool any = t_lo < n_tiles;
+        if (any) {
+            P::template load_k<true, MAPPED>(kp, t_lo, kr);
+            V::template load<true, MAPPED>(vp, c.NK, t_lo, vr);
+        }
+        P::load_q(a, c, qw0 + lq, logit_scale, q);
+        if (any) {
+            P::commit_k(kr, kbuf(t_lo));
+            V::commit(vr, vbuf(t_lo));
+        }
+        if (t_lo + 1 < n_tiles) {
+            P::template load_k<true, MAPPED>(kp, t_lo + 1, kr);
+            P::commit_k(kr, kbuf(t_lo + 1));
+            V::template load<true, MAPPED>(vp, c.NK, t_lo + 1, vr);
+        }
+        if (t_lo + 2 < n_tiles) P::template load_k<true, MAPPED>(kp, t_lo + 2, kr);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+        m_run = kNegInf;
+        l_a = 0.f;
+        l_b = 0.f;
+        __syncthreads();
+        float s[32];
+        if (any) qk_tile<false>(t_lo, s);
+
+        const bool lagging = w >= 4;  // waves w and w + 4 share a SIMD
+        if (lagging) __syncthreads();
+        int t = t_lo;
+        const int t_steady = SPLIT ? min(n_full, n_tiles) : n_full;
+        // Steady tiles load K(t+3) and V(t+2) unclamped and run an unmasked
+        // softmax: t+3 must lie below n_full.
+        for (; t + 3 < t_steady; ++t) {
+            uint32_t pk[16];
+            vector_phase<true>(t, s, pk);
+            phase_barrier();
+            matrix_phase<true>(t, 2, pk, s);
+            phase_barrier();
+        }
+        for (; t < n_tiles; ++t) {
+            uint32_t pk[16];
+            const int na = vector_phase<false>(t, s, pk);
+            phase_barrier();
+            matrix_phase<false>(t, na, pk, s);
+            phase_barrier();
+        }
+        if (!lagging) __syncthreads();
+        finish(a);
+    }
+
+    // Normalised O (or the split-K partial) of the wave's rows.
+    __device__ __forceinline__ void finish(const RunArgs& a) {
+        if (qw0 >= c.S) return;
+        if (SPLIT) {
+            // A row that saw no key of this split (its first tile starts past
+            // the row) keeps m_run = -inf; its partial is written empty.
+            const bool seen = m_run != kNegInf;
+            const float l_all = halves_sum(l_a + l_b);  // cross-lane: every lane takes part
+            const float l = seen ? l_all : 0.f;
+            const int qi = qw0 + lq;
+            if (qi < c.S) {
+                const size_t row = q_index(a, c, qi, D) / D;
+                float* dst = split_o(a, row, c.split, D);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<float4*>(dst + 32 * db + 8 * g + 4 * lh) =
+                            seen ? make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3])
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+                if (lh == 0) *split_ml(a, row, c.split, D) = make_float2(m_run, l);
+            }
+            return;
+        }
+        const float inv = PWL ? newton_reciprocal(halves_sum(l_a + l_b)) : 1.0f / halves_sum(l_a + l_b);
+        const int qi = qw0 + lq;
+        if (qi < c.S) {
+            float* orow = a.out + q_index(a, c, qi, D);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 val = make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
+                                                   o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                    *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * lh) = val;
+                }
+        }
+    }
+
     __device__ __forceinline__ void run(const RunArgs& a, float logit_scale) {
         const int lane = threadIdx.x & 63;
         const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -1071,7 +1240,7 @@ struct FusedAttn {
         kq0 = c.kshift + qw0;
         const int n_all = (c.kshift + min(c.q0 + BMW, c.S) + BN - 1) / BN;
         const int n_full = min((c.kshift + c.q0) / BN, n_all);  // tiles every query of the workgroup sees whole
-        int t_lo = 0;
+        t_lo = 0;
         n_tiles = n_all;
         if (SPLIT) {
             const int per = (n_all + a.n_split - 1) / a.n_split;
@@ -1140,43 +1309,14 @@ struct FusedAttn {
             if (t + 1 < n_tiles) step<false>(t + 1, sb, sa);
         }
 
-        if (qw0 >= c.S) return;
-        if (SPLIT) {
-            const float l = halves_sum(l_a + l_b);
-            const int qi = qw0 + lq;
-            if (qi < c.S) {
-                const size_t row = q_index(a, c, qi, D) / D;
-                float* dst = split_o(a, row, c.split, D);
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        *reinterpret_cast<float4*>(dst + 32 * db + 8 * g + 4 * lh) =
-                            make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
-                if (lh == 0) *split_ml(a, row, c.split, D) = make_float2(m_run, l);
-            }
-            return;
-        }
-        const float inv = PWL ? newton_reciprocal(halves_sum(l_a + l_b)) : 1.0f / halves_sum(l_a + l_b);
-        const int qi = qw0 + lq;
-        if (qi < c.S) {
-            float* orow = a.out + q_index(a, c, qi, D);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 val = make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
-                                                   o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                    *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * lh) = val;
-                }
-        }
+        finish(a);
     }
 };
 
 template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, int MINB, bool MAPPED,
-          bool SPLIT = false, bool PWL = false>
+          bool SPLIT = false, bool PWL = false, bool PP = false>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, float logit_scale) {
-    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT, PWL>;
+    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT, PWL, PP>;
     __shared__ __attribute__((aligned(16))) char lds[K::kLds];
     __shared__ float knots[PWL ? 9 : 1];
     K k;
@@ -1196,7 +1336,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, floa
             zero_rows<D, K::BMW, K::NT>(a, k.c);
         return;
     }
-    k.run(a, logit_scale);
+    if (PP)
+        k.run_pp(a, logit_scale);
+    else
+        k.run(a, logit_scale);
 }
 
 // ------------------------------------------------ fp32 kernel (fp32 matrix cores)
@@ -1436,8 +1579,10 @@ void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
     if (prefill_uses_eight_waves(a)) {
         dim3 g = grid_for(a, 256);
         g.x *= ns;
-        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP>), g, dim3(512), 0, s, a,
-                           a.score_scale * kLog2e);
+        // head_dim 128 plain prefill runs the two-group schedule (measured
+        // faster there; slower for 64 and 96, whose waves hold fewer registers).
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP, false, D == 128 && !M && !SP>), g,
+                           dim3(512), 0, s, a, a.score_scale * kLog2e);
     } else {
         dim3 g = grid_for(a, 128);
         g.x *= ns;
