@@ -60,6 +60,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int BM = 32 * kWaves;  // query rows per workgroup
 constexpr int BN = 64;           // keys per LDS tile
+constexpr int kMinSplitTiles = 4;  // split-K: fewest key tiles per non-empty split
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8 between rescales
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -1086,6 +1087,24 @@ struct FusedAttn {
         __syncthreads();
     }
 
+    // Split-K: the workgroup's n_all key tiles are cut into as many equal
+    // ranges of at least kMinSplitTiles tiles as the launch's split count
+    // allows; this split's range is [t_lo, n_tiles), empty past that count.
+    // A short prefix thus runs on few splits and writes few partials.
+    __device__ __forceinline__ void split_range(const RunArgs& a, int n_all) {
+        const int eff = max(1, min(a.n_split, n_all / kMinSplitTiles));
+        const int per = (n_all + eff - 1) / eff;
+        t_lo = min(c.split * per, n_all);
+        n_tiles = min(t_lo + per, n_all);
+    }
+    // The partial of a row that saw no key: (max, sum) = (-inf, 0); its O part
+    // is not written (the merge reads O only for a finite max).
+    __device__ __forceinline__ void empty_partials(const RunArgs& a) const {
+        const int qi = qw0 + lq;
+        if (qi < c.S && lh == 0)
+            *split_ml(a, q_index(a, c, qi, D) / D, c.split, D) = make_float2(kNegInf, 0.f);
+    }
+
     // Two-group schedule (eight waves).  Each tile t is split into two phases
     // separated by workgroup barriers:
     //   vector phase t: commit K(t+2) -> K' and V(t+1) -> V^T (registers loaded
@@ -1133,9 +1152,11 @@ struct FusedAttn {
         t_lo = 0;
         n_tiles = n_all;
         if (SPLIT) {
-            const int per = (n_all + a.n_split - 1) / a.n_split;
-            t_lo = min(c.split * per, n_all);
-            n_tiles = min(t_lo + per, n_all);
+            split_range(a, n_all);
+            if (t_lo >= n_tiles) {  // empty split (workgroup-uniform): no barrier has run yet
+                empty_partials(a);
+                return;
+            }
         }
         kp = P::template kptr<MAPPED>(a, c);
         vp = kv_rows<MAPPED>(a, c, a.v, D, 2);
@@ -1197,10 +1218,12 @@ struct FusedAttn {
         if (qw0 >= c.S) return;
         if (SPLIT) {
             // A row that saw no key of this split (its first tile starts past
-            // the row) keeps m_run = -inf; its partial is written empty.
-            const bool seen = m_run != kNegInf;
-            const float l_all = halves_sum(l_a + l_b);  // cross-lane: every lane takes part
-            const float l = seen ? l_all : 0.f;
+            // the row) keeps m_run = -inf: an empty partial.
+            const float l = halves_sum(l_a + l_b);  // cross-lane: every lane takes part
+            if (m_run == kNegInf) {
+                empty_partials(a);
+                return;
+            }
             const int qi = qw0 + lq;
             if (qi < c.S) {
                 const size_t row = q_index(a, c, qi, D) / D;
@@ -1210,8 +1233,7 @@ struct FusedAttn {
 #pragma unroll
                     for (int g = 0; g < 4; ++g)
                         *reinterpret_cast<float4*>(dst + 32 * db + 8 * g + 4 * lh) =
-                            seen ? make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3])
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+                            make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
                 if (lh == 0) *split_ml(a, row, c.split, D) = make_float2(m_run, l);
             }
             return;
@@ -1243,9 +1265,11 @@ struct FusedAttn {
         t_lo = 0;
         n_tiles = n_all;
         if (SPLIT) {
-            const int per = (n_all + a.n_split - 1) / a.n_split;
-            t_lo = min(c.split * per, n_all);
-            n_tiles = min(t_lo + per, n_all);
+            split_range(a, n_all);
+            if (t_lo >= n_tiles) {  // empty split (workgroup-uniform): no barrier has run yet
+                empty_partials(a);
+                return;
+            }
         }
         kp = P::template kptr<MAPPED>(a, c);
         vp = kv_rows<MAPPED>(a, c, a.v, D, 2);

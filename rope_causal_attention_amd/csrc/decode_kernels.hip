@@ -306,13 +306,13 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     for (int s = 0; s < a.n_split; ++s) {
         const size_t part = bh * a.n_split + s;
         const float2 st = *reinterpret_cast<const float2*>(ml + 2 * part);
+        if (st.x == kNegInf) continue;  // empty split: its O part is not read (may be unwritten)
         float o[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int d = threadIdx.x + 64 * i;
             o[i] = d < D ? a.ws[part * D + d] : 0.f;
         }
-        if (st.x == kNegInf) continue;  // empty split
         const float M2 = fmaxf(M, st.x);
         const float f_old = weight(M, M2), f_new = __builtin_amdgcn_exp2f(st.x - M2);
         L = L * f_old + st.y * f_new;
