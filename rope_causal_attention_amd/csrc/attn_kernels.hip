@@ -885,15 +885,22 @@ struct VStage8 : VStage<D, NT> {
 // key tiles finds each row's maximum logit, the main loop then weights every
 // key by the chord approximation of exp relative to that maximum.
 // PP: the two-group schedule of run_pp (eight waves, three LDS buffers).
+// PAIR: one barrier per two tiles (four LDS buffers each for K' and V^T, K
+// staged three tiles ahead and V two): a buffer is rewritten only after the
+// barrier that follows its last read, and a tile is whole one barrier before
+// it is read.
 template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, bool MAPPED, bool SPLIT,
-          bool PWL = false, bool PP = false>
+          bool PWL = false, bool PP = false, bool PAIR = false>
 struct FusedAttn {
     static constexpr int NT = 64 * NW;
     static constexpr int BMW = 32 * NW;
     using P = QKT<D, NT>;
     using V = VST<D, NT>;
     static_assert(!PP || (NW == 8 && !PWL), "the two-group schedule needs eight waves");
-    static constexpr int kBufs = PP ? 3 : 2;
+    static_assert(!(PP && PAIR), "one schedule at a time");
+    static constexpr int kBufs = PP ? 3 : (PAIR ? 4 : 2);
+    static constexpr int KA = PAIR ? 3 : 2;  // K staged KA tiles ahead of the softmax tile
+    static constexpr int VA = PAIR ? 2 : 1;  // V staged VA tiles ahead
     static constexpr int kLds = kBufs * (P::kBytes + V::kBytes);
 
     char* lds;
@@ -908,7 +915,7 @@ struct FusedAttn {
     f32x16 o[D / 32];
     float m_run, l_a, l_b;
 
-    __device__ __forceinline__ int slot(int t) const { return PP ? (t - t_lo) % 3 : (t & 1); }
+    __device__ __forceinline__ int slot(int t) const { return PP ? (t - t_lo) % 3 : PAIR ? ((t - t_lo) & 3) : (t & 1); }
     __device__ __forceinline__ char* kbuf(int t) const { return lds + slot(t) * P::kBytes; }
     __device__ __forceinline__ _Float16* vbuf(int t) const {
         return reinterpret_cast<_Float16*>(lds + kBufs * P::kBytes + slot(t) * V::kBytes);
@@ -1066,12 +1073,13 @@ struct FusedAttn {
     }
 
     // One pipeline step for tile t; s holds S(t) on entry, sn receives S(t+1).
+    // bar: end with a workgroup barrier (always, unless PAIR).
     template <bool STEADY>
-    __device__ __forceinline__ void step(int t, float* s, float* sn) {
-        const bool ld_k = STEADY || t + 2 < n_tiles;
-        const bool ld_v = STEADY || t + 1 < n_tiles;
-        if (ld_k) P::template load_k<!STEADY, MAPPED>(kp, t + 2, kr);
-        if (ld_v) V::template load<!STEADY, MAPPED>(vp, c.NK, t + 1, vr);
+    __device__ __forceinline__ void step(int t, float* s, float* sn, bool bar = true) {
+        const bool ld_k = STEADY || t + KA < n_tiles;
+        const bool ld_v = STEADY || t + VA < n_tiles;
+        if (ld_k) P::template load_k<!STEADY, MAPPED>(kp, t + KA, kr);
+        if (ld_v) V::template load<!STEADY, MAPPED>(vp, c.NK, t + VA, vr);
         const int na = STEADY ? 2 : nact(t);
         uint32_t pk[16];
         if (na > 0) {
@@ -1080,11 +1088,11 @@ struct FusedAttn {
             else
                 softmax<STEADY>(t, na, s, pk);
         }
-        if (ld_v) qk_tile<STEADY>(t + 1, sn);
+        if (STEADY || t + 1 < n_tiles) qk_tile<STEADY>(t + 1, sn);
         if (na > 0) pv_tile(t, na, pk);
-        if (ld_k) P::commit_k(kr, kbuf(t));
-        if (ld_v) V::commit(vr, vbuf(t + 1));
-        __syncthreads();
+        if (ld_k) P::commit_k(kr, kbuf(t + KA));
+        if (ld_v) V::commit(vr, vbuf(t + VA));
+        if (!PAIR || bar) __syncthreads();
     }
 
     // Split-K: the workgroup's n_all key tiles are cut into as many equal
@@ -1309,6 +1317,14 @@ struct FusedAttn {
             P::template load_k<true, MAPPED>(kp, t_lo + 1, kr);
             P::commit_k(kr, kbuf(t_lo + 1));
         }
+        if (PAIR && t_lo + 1 < n_tiles) {
+            V::template load<true, MAPPED>(vp, c.NK, t_lo + 1, vr);
+            V::commit(vr, vbuf(t_lo + 1));
+        }
+        if (PAIR && t_lo + 2 < n_tiles) {
+            P::template load_k<true, MAPPED>(kp, t_lo + 2, kr);
+            P::commit_k(kr, kbuf(t_lo + 2));
+        }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
         m_run = PWL ? pwl_max : kNegInf;
@@ -1324,13 +1340,15 @@ struct FusedAttn {
         // below n_full (tile n_full itself may reach past the last key) and in range.
         int t = t_lo;
         const int t_steady = SPLIT ? min(n_full, n_tiles) : n_full;
-        for (; t + 3 < t_steady; t += 2) {
-            step<true>(t, sa, sb);
-            step<true>(t + 1, sb, sa);
+        // (PAIR: a steady pair stages K(t+4) and V(t+3), so t+4 lies below n_full.)
+        for (; t + KA + 1 < t_steady; t += 2) {
+            step<true>(t, sa, sb, false);
+            step<true>(t + 1, sb, sa, true);
         }
         for (; t < n_tiles; t += 2) {
-            step<false>(t, sa, sb);
-            if (t + 1 < n_tiles) step<false>(t + 1, sb, sa);
+            const bool two = t + 1 < n_tiles;
+            step<false>(t, sa, sb, !two);
+            if (two) step<false>(t + 1, sb, sa, true);
         }
 
         finish(a);
@@ -1338,9 +1356,9 @@ struct FusedAttn {
 };
 
 template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, int MINB, bool MAPPED,
-          bool SPLIT = false, bool PWL = false, bool PP = false>
+          bool SPLIT = false, bool PWL = false, bool PP = false, bool PAIR = false>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, float logit_scale) {
-    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT, PWL, PP>;
+    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT, PWL, PP, PAIR>;
     __shared__ __attribute__((aligned(16))) char lds[K::kLds];
     __shared__ float knots[PWL ? 9 : 1];
     K k;
@@ -1605,8 +1623,9 @@ void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
         g.x *= ns;
         // head_dim 128 plain prefill runs the two-group schedule (measured
         // faster there; slower for 64 and 96, whose waves hold fewer registers).
-        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP, false, D == 128 && !M && !SP>), g,
-                           dim3(512), 0, s, a, a.score_scale * kLog2e);
+        constexpr bool kPP = D == 128 && !M && !SP;
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP, false, kPP, !kPP>), g, dim3(512), 0,
+                           s, a, a.score_scale * kLog2e);
     } else {
         dim3 g = grid_for(a, 128);
         g.x *= ns;
