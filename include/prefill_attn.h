@@ -171,6 +171,9 @@ int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int batch, int 
  * article, §三.3, uses to combine blocks of the online softmax).  n_split = 0
  * lets the library choose; a NULL or short workspace lowers n_split to what fits,
  * down to 1, which is prefill_attn_run_cached.  PA_IN_F32 always runs unsplit.
+ * n_split is an upper bound: each (query block, sequence, head) uses only as
+ * many splits as give every split at least four 64-key tiles of its own keys.
+ * The workspace contents are scratch between calls (nothing needs clearing).
  * Results equal prefill_attn_run_cached's up to the rounding of the merge.
  */
 size_t prefill_attn_run_cached_workspace_size(const prefill_attn* h, int batch, int seq_len, int n_split);
