@@ -1623,9 +1623,11 @@ void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
         g.x *= ns;
         // head_dim 128 plain prefill runs the two-group schedule (measured
         // faster there; slower for 64 and 96, whose waves hold fewer registers).
+        // Split launches keep one barrier per tile: their short key ranges
+        // would pay the deeper prologue of the paired schedule.
         constexpr bool kPP = D == 128 && !M && !SP;
-        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP, false, kPP, !kPP>), g, dim3(512), 0,
-                           s, a, a.score_scale * kLog2e);
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP, false, kPP, !kPP && !SP>), g,
+                           dim3(512), 0, s, a, a.score_scale * kLog2e);
     } else {
         dim3 g = grid_for(a, 128);
         g.x *= ns;
