@@ -146,7 +146,7 @@ def bench_decode(args, torch, pa):
     stream = torch.cuda.current_stream()
 
     def step():
-        attn.decode(q, kc, vc, kv_map, pos_offsets=pos, workspace=ws, out=out, stream=stream)
+        attn.decode(q, kc, vc, kv_map, pos_offsets=pos, workspace=ws, out=out, stream=stream, n_split=args.n_split)
 
     for _ in range(args.warmup):
         step()
@@ -193,6 +193,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=1024, help="chunk length for --mode chunked")
     ap.add_argument("--pwl-softmax", action="store_true",
                     help="int16 workload with the piecewise-linear softmax (PA_IN_I16_PWL)")
+    ap.add_argument("--split", dest="n_split", type=int, default=0,
+                    help="split count for --mode chunked / decode (0 = chosen by the library)")
     ap.add_argument("--no-split", dest="split", action="store_false",
                     help="--mode chunked without split-K over the cached keys")
     args = ap.parse_args()
@@ -233,14 +235,16 @@ def main():
                    kd[:, p:p + n].contiguous(), vd[:, p:p + n].contiguous()) for p, n in chunks]
         outs = [torch.empty(x[1].shape, dtype=torch.float32, device="cuda") for x in pieces]
         # Split-K over the cached keys (the library picks the split), workspace for up to 16 splits.
-        ws = torch.empty(pa.prefill_attn_run_cached_workspace_size(attn.handle, B, args.chunk, 16),
+        ws = torch.empty(pa.prefill_attn_run_cached_workspace_size(attn.handle, B, args.chunk,
+                                                                   max(16, args.n_split)),
                          dtype=torch.uint8, device="cuda")
 
         def step():
             for (off, qc, kn, vn), oc in zip(pieces, outs):
                 attn.kv_cache_update(kn, vn, kc, vc, kv_map, off, stream=stream)
                 attn.run_cached(qc, kc, vc, kv_map, pos_offsets=off, score_scale=w.score_scale, out=oc,
-                                stream=stream, n_split=0 if args.split else 1, workspace=ws if args.split else None)
+                                stream=stream, n_split=args.n_split if args.split else 1,
+                                workspace=ws if args.split else None)
 
     for _ in range(args.warmup):
         step()

@@ -248,9 +248,11 @@ extern "C" int prefill_attn_run_cached_splitk(const prefill_attn* h, int in_dtyp
     if (in_dtype == PA_IN_F32 || batch <= 0 || seq_len <= 0) n_split = 1;  // fp32 kernel has no split
     if (n_split == 0) {
         // Split only a grid that leaves CUs idle (under 256 eight-wave workgroups):
-        // aim at two rounds of them, at least four 64-key tiles per split.
+        // aim at one round of them (one per CU; a second round doubled the
+        // partials to merge and measured slower), at least four 64-key tiles
+        // per split.
         const long long wgs256 = static_cast<long long>((seq_len + 255) / 256) * batch * h->n_heads;
-        n_split = wgs256 >= 256 ? 1 : static_cast<int>((512 + wgs256 - 1) / wgs256);
+        n_split = wgs256 >= 256 ? 1 : static_cast<int>((256 + wgs256 - 1) / wgs256);
         n_split = std::min(n_split, std::max(1, map_stride / (4 * 64)));
     }
     if (n_split > 1 && (!workspace || workspace_bytes < split_ws_bytes(h, batch, seq_len, 2))) n_split = 1;
