@@ -215,6 +215,7 @@ def _chunked(attn, q, k, v, chunks, kv_map, n_slots, dt, scale):
 
 @pytest.mark.parametrize("name,B,Hq,Hkv,D,chunks", [
     ("chunk_8wave_d128", 4, 32, 8, 128, [512, 512, 512]),
+    ("chunk_8wave_d96", 2, 32, 32, 96, [1024, 1024]),  # paired-barrier schedule at head_dim 96
     ("chunk_8wave_odd_tiles", 4, 32, 8, 128, [320, 704]),  # prefix 320: an odd count of whole tiles
     ("chunk_ragged_d64", 2, 8, 2, 64, [100, 333, 1, 250]),
 ])
