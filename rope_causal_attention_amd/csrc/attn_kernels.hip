@@ -1510,33 +1510,36 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(RunArgs a, float
 // ------------------------------------------------ KV cache update
 
 // New token i of sequence b (logical position off[b] + i) is copied to slot
-// kv_map[b][off[b] + i] of the caches; nothing else is touched.  One thread
-// moves 16 bytes of K and 16 bytes of V.  A sequence whose chunk leaves the
-// map row, or a slot outside [0, n_slots), is skipped and sets the status word.
+// kv_map[b][off[b] + i] of the caches; nothing else is touched.  One
+// workgroup per new token: the offset and the slot are looked up once, then
+// the K and V rows are copied in 16-byte chunks.  A sequence whose chunk
+// leaves the map row, or a slot outside [0, n_slots), is skipped and sets the
+// status word.
 __global__ __launch_bounds__(kThreads) void kv_cache_update_kernel(RunArgs a, uint32_t row_bytes, char* dk,
                                                                    char* dv) {
-    const uint32_t chunks = row_bytes / 16;
-    const size_t g = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
-    const size_t tok = g / chunks;
-    if (tok >= static_cast<size_t>(a.batch) * a.seq_len) return;
-    const uint32_t ch = static_cast<uint32_t>(g % chunks);
-    const int b = static_cast<int>(tok / a.seq_len), i = static_cast<int>(tok % a.seq_len);
+    const uint32_t tok = blockIdx.x;  // < batch * seq_len (checked at launch)
+    const int b = static_cast<int>(tok / static_cast<uint32_t>(a.seq_len));
+    const int i = static_cast<int>(tok - static_cast<uint32_t>(b) * static_cast<uint32_t>(a.seq_len));
     const int off = a.pos_offsets ? a.pos_offsets[b] : 0;
     if (off < 0 || static_cast<long long>(off) + a.seq_len > a.map_stride) {
-        if (ch == 0) atomicOr(a.status, 1);
+        if (threadIdx.x == 0) atomicOr(a.status, 1);
         return;
     }
     const int slot = a.kv_map[static_cast<size_t>(b) * a.map_stride + off + i];
     if (static_cast<unsigned>(slot) >= static_cast<unsigned>(a.n_slots)) {
-        if (ch == 0) atomicOr(a.status, 1);
+        if (threadIdx.x == 0) atomicOr(a.status, 1);
         return;
     }
-    const size_t src = tok * row_bytes + 16u * ch;
-    const size_t dst = static_cast<size_t>(slot) * row_bytes + 16u * ch;
-    const uint4 kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k) + src);
-    const uint4 vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) + src);
-    *reinterpret_cast<uint4*>(dk + dst) = kx;
-    *reinterpret_cast<uint4*>(dv + dst) = vx;
+    const char* ks = static_cast<const char*>(a.k) + static_cast<size_t>(tok) * row_bytes;
+    const char* vs = static_cast<const char*>(a.v) + static_cast<size_t>(tok) * row_bytes;
+    char* kd = dk + static_cast<size_t>(slot) * row_bytes;
+    char* vd = dv + static_cast<size_t>(slot) * row_bytes;
+    for (uint32_t c = 16u * threadIdx.x; c < row_bytes; c += 16u * kThreads) {
+        const uint4 kx = *reinterpret_cast<const uint4*>(ks + c);
+        const uint4 vx = *reinterpret_cast<const uint4*>(vs + c);
+        *reinterpret_cast<uint4*>(kd + c) = kx;
+        *reinterpret_cast<uint4*>(vd + c) = vx;
+    }
 }
 
 // ------------------------------------------------ int16 test kernels
@@ -1710,8 +1713,7 @@ hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t s) { PA_D
 
 hipError_t launch_kv_cache_update(int head_dim, int el, const RunArgs& a, void* dst_k, void* dst_v, hipStream_t s) {
     const uint32_t row_bytes = static_cast<uint32_t>(a.n_kv_heads) * head_dim * el;
-    const size_t chunks = static_cast<size_t>(a.batch) * a.seq_len * (row_bytes / 16);
-    const size_t blocks = (chunks + kThreads - 1) / kThreads;
+    const size_t blocks = static_cast<size_t>(a.batch) * a.seq_len;  // one workgroup per new token
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffu) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kv_cache_update_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a,
