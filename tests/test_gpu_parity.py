@@ -61,6 +61,7 @@ PINGPONG_CASES = [
     ("pp_d96_ragged_gqa", 2, 32, 16, 1100, 96, 1e4, [0, 37]),
     ("pp_d128_ragged", 2, 32, 32, 1030, 128, 1e6, None),
     ("pp_d64_exact", 1, 64, 8, 1024, 64, 1e4, [5]),
+    ("pp_d128_gqa4_offsets", 2, 32, 8, 1100, 128, 1e4, [0, 300]),  # two-group schedule, GQA 4, offsets
 ]
 
 
