@@ -1626,15 +1626,20 @@ void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
         g.x *= ns;
         // head_dim 128 plain prefill runs the two-group schedule (measured
         // faster there; slower for 64 and 96, whose waves hold fewer registers).
-        // Split launches keep one barrier per tile: their short key ranges
-        // would pay the deeper prologue of the paired schedule.
-        constexpr bool kPP = D == 128 && !M && !SP;
+        // head_dim 128 runs the two-group schedule (its single S buffer keeps
+        // the kernel out of spills, cached and split launches included).
+        // Split launches otherwise keep one barrier per tile: their short key
+        // ranges would pay the deeper prologue of the paired schedule.
+        constexpr bool kPP = D == 128;
         hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP, false, kPP, !kPP && !SP>), g,
                            dim3(512), 0, s, a, a.score_scale * kLog2e);
     } else {
         dim3 g = grid_for(a, 128);
         g.x *= ns;
-        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16QK, VStage, 4, 2, M, SP>), g, dim3(256), 0, s, a,
+        // Two workgroups per CU fit only head_dim 64 in 256 VGPRs; at 96 and 128
+        // the whole-tile staging registers spilled (up to 400 bytes per lane)
+        // and one workgroup per CU, with the accumulators in AGPRs, is faster.
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16QK, VStage, 4, D == 64 ? 2 : 1, M, SP>), g, dim3(256), 0, s, a,
                            a.score_scale * kLog2e);
     }
 }

@@ -356,6 +356,7 @@ SPLIT_CASES = [
     ("sk_bf16_d96_ring_auto", 1, 4, 4, 96, "bf16", 1e4, [2000], 100, "ring", 4096, 0),
     ("sk_bf16_d64_many", 2, 4, 2, 64, "bf16", 1e4, [64, 5], 77, "paged", 1024, 9),
     ("sk_i16_d128", 1, 4, 2, 128, "i16", 1e4, [900], 128, "paged", 2048, 3),
+    ("sk_bf16_d128_8wave", 1, 32, 8, 128, "bf16", 1e4, [1500], 256, "paged", 2048, 8),  # two-group split
 ]
 
 
