@@ -41,6 +41,8 @@
 //  * fp32 variant: v_mfma_f32_32x32x2_f32 for both products, fp32 LDS tiles.
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include "internal.h"
@@ -136,6 +138,24 @@ __device__ __forceinline__ BlockPos map_block(int n_qblocks, int batch, int n_he
     return {qb, bh / n_heads, bh % n_heads};
 }
 
+// Paired order: workgroup bid owns pair j of one (batch, head), the query
+// blocks n_qblocks - 1 - j (item 0) and j (item 1), with the same
+// XCD-contiguous (batch, head) ranges as map_block.  With an odd block count
+// the middle block forms a pair of its own (item 1 is then skipped).
+__device__ __forceinline__ BlockPos map_pair(int n_qblocks, int batch, int n_heads, int bid, int item) {
+    const int BH = batch * n_heads;
+    int j, bh;
+    if ((BH & 7) == 0) {
+        const int x = bid & 7, jj = bid >> 3, hpx = BH >> 3;
+        j = jj / hpx;
+        bh = x * hpx + jj % hpx;
+    } else {
+        j = bid / BH;
+        bh = bid % BH;
+    }
+    return {item == 0 ? n_qblocks - 1 - j : j, bh / n_heads, bh % n_heads};
+}
+
 // Query i of the workgroup's (batch, head) has table position off + i.  Keys
 // are numbered in key space: key j has table position koff + j, the keys a
 // query i sees are j <= kshift + i, and there are NK = kshift + S keys.
@@ -148,12 +168,10 @@ struct Ctx {
     int split;  // this workgroup's key range among n_split (split-K only)
 };
 
-template <int BM, bool MAPPED, bool SPLIT = false>
-__device__ __forceinline__ bool make_ctx(const RunArgs& a, Ctx& c) {
-    const int n_qblocks = (a.seq_len + BM - 1) / BM;
-    const int bid = SPLIT ? static_cast<int>(blockIdx.x) / a.n_split : static_cast<int>(blockIdx.x);
-    c.split = SPLIT ? static_cast<int>(blockIdx.x) % a.n_split : 0;
-    const BlockPos bp = map_block(n_qblocks, a.batch, a.n_heads, bid);
+// Context of query block bp; false when the sequence's positions leave the table.
+template <int BM, bool MAPPED>
+__device__ __forceinline__ bool make_ctx_at(const RunArgs& a, const BlockPos& bp, int split, Ctx& c) {
+    c.split = split;
     c.b = bp.b;
     c.hq = bp.hq;
     c.hkv = bp.hq / (a.n_heads / a.n_kv_heads);
@@ -165,6 +183,14 @@ __device__ __forceinline__ bool make_ctx(const RunArgs& a, Ctx& c) {
     c.NK = c.kshift + c.S;
     const long long end = static_cast<long long>(c.off) + a.seq_len;
     return c.off >= 0 && end <= a.max_seq && (!MAPPED || end <= a.map_stride);
+}
+
+template <int BM, bool MAPPED, bool SPLIT = false>
+__device__ __forceinline__ bool make_ctx(const RunArgs& a, Ctx& c) {
+    const int n_qblocks = (a.seq_len + BM - 1) / BM;
+    const int bid = SPLIT ? static_cast<int>(blockIdx.x) / a.n_split : static_cast<int>(blockIdx.x);
+    const int split = SPLIT ? static_cast<int>(blockIdx.x) % a.n_split : 0;
+    return make_ctx_at<BM, MAPPED>(a, map_block(n_qblocks, a.batch, a.n_heads, bid), split, c);
 }
 
 __device__ __forceinline__ size_t q_index(const RunArgs& a, const Ctx& c, int i, int D) {
@@ -1172,22 +1198,26 @@ struct FusedAttn {
         // Prologue: K'(t_lo), K'(t_lo+1) and V^T(t_lo) in LDS; K(t_lo+2) and
         // V(t_lo+1) in registers for the first vector phase.  An empty split
         // loads nothing (a clamped row past the last key would be negative).
+        // All loads are issued before any commit (one memory round trip); K(t_lo+2)
+        // and V(t_lo+1) stay in kr / vr for the first vector phase.
         const bool any = t_lo < n_tiles;
+        typename P::KRegs kr0, kr1;
+        typename V::Regs vr0;
         if (any) {
-            P::template load_k<true, MAPPED>(kp, t_lo, kr);
-            V::template load<true, MAPPED>(vp, c.NK, t_lo, vr);
-        }
-        P::load_q(a, c, qw0 + lq, logit_scale, q);
-        if (any) {
-            P::commit_k(kr, kbuf(t_lo));
-            V::commit(vr, vbuf(t_lo));
+            P::template load_k<true, MAPPED>(kp, t_lo, kr0);
+            V::template load<true, MAPPED>(vp, c.NK, t_lo, vr0);
         }
         if (t_lo + 1 < n_tiles) {
-            P::template load_k<true, MAPPED>(kp, t_lo + 1, kr);
-            P::commit_k(kr, kbuf(t_lo + 1));
+            P::template load_k<true, MAPPED>(kp, t_lo + 1, kr1);
             V::template load<true, MAPPED>(vp, c.NK, t_lo + 1, vr);
         }
         if (t_lo + 2 < n_tiles) P::template load_k<true, MAPPED>(kp, t_lo + 2, kr);
+        P::load_q(a, c, qw0 + lq, logit_scale, q);
+        if (any) {
+            P::commit_k(kr0, kbuf(t_lo));
+            V::commit(vr0, vbuf(t_lo));
+        }
+        if (t_lo + 1 < n_tiles) P::commit_k(kr1, kbuf(t_lo + 1));
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
         m_run = kNegInf;
@@ -1303,28 +1333,27 @@ struct FusedAttn {
 
         // An empty split (t_lo == n_all) loads no tile: a clamped row of a tile
         // past the last key would be negative, and row offsets are unsigned.
+        // Every load of the first tiles (and Q's) is issued before any of them
+        // is committed, so the prologue waits for one memory round trip.
         const bool any = !SPLIT || t_lo < n_tiles;
+        const bool k1 = t_lo + 1 < n_tiles, v1 = PAIR && t_lo + 1 < n_tiles, k2 = PAIR && t_lo + 2 < n_tiles;
+        typename P::KRegs kr1, kr2;
+        typename V::Regs vr1;
         if (any) {
             P::template load_k<true, MAPPED>(kp, t_lo, kr);
             V::template load<true, MAPPED>(vp, c.NK, t_lo, vr);
         }
+        if (k1) P::template load_k<true, MAPPED>(kp, t_lo + 1, kr1);
+        if (v1) V::template load<true, MAPPED>(vp, c.NK, t_lo + 1, vr1);
+        if (k2) P::template load_k<true, MAPPED>(kp, t_lo + 2, kr2);
         P::load_q(a, c, qw0 + lq, logit_scale, q);
         if (any) {
             P::commit_k(kr, kbuf(t_lo));
             V::commit(vr, vbuf(t_lo));
         }
-        if (t_lo + 1 < n_tiles) {
-            P::template load_k<true, MAPPED>(kp, t_lo + 1, kr);
-            P::commit_k(kr, kbuf(t_lo + 1));
-        }
-        if (PAIR && t_lo + 1 < n_tiles) {
-            V::template load<true, MAPPED>(vp, c.NK, t_lo + 1, vr);
-            V::commit(vr, vbuf(t_lo + 1));
-        }
-        if (PAIR && t_lo + 2 < n_tiles) {
-            P::template load_k<true, MAPPED>(kp, t_lo + 2, kr);
-            P::commit_k(kr, kbuf(t_lo + 2));
-        }
+        if (k1) P::commit_k(kr1, kbuf(t_lo + 1));
+        if (v1) V::commit(vr1, vbuf(t_lo + 1));
+        if (k2) P::commit_k(kr2, kbuf(t_lo + 2));
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
         m_run = PWL ? pwl_max : kNegInf;
@@ -1371,13 +1400,33 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, floa
                                  0.0009118819655545162f, 0.00033546262790251185f};
         knots[threadIdx.x] = kE[threadIdx.x];
     }
-    if (!make_ctx<K::BMW, MAPPED, SPLIT>(a, k.c)) {
+    // One query block, or two in a paired launch (eight-wave kernels only).
+    const bool paired = !SPLIT && NW == 8 && a.paired;
+    const int n_qblocks = (a.seq_len + K::BMW - 1) / K::BMW;
+    const int bid = SPLIT ? static_cast<int>(blockIdx.x) / a.n_split : static_cast<int>(blockIdx.x);
+    const int split = SPLIT ? static_cast<int>(blockIdx.x) % a.n_split : 0;
+    const BlockPos bp = paired ? map_pair(n_qblocks, a.batch, a.n_heads, bid, 0)
+                               : map_block(n_qblocks, a.batch, a.n_heads, bid);
+    const bool ok = make_ctx_at<K::BMW, MAPPED>(a, bp, split, k.c);
+    if (!ok) {
         if (SPLIT)
             zero_partials<D, K::BMW, K::NT>(a, k.c);
         else
             zero_rows<D, K::BMW, K::NT>(a, k.c);
+    } else if (PP) {
+        k.run_pp(a, logit_scale);
+    } else {
+        k.run(a, logit_scale);
+    }
+    if (!paired || 2 * bp.qb == n_qblocks - 1) return;  // the middle block of an odd count runs alone
+    // Second block of the pair: same (batch, head), so the same validity.
+    const BlockPos bp2 = map_pair(n_qblocks, a.batch, a.n_heads, bid, 1);
+    make_ctx_at<K::BMW, MAPPED>(a, bp2, split, k.c);
+    if (!ok) {
+        zero_rows<D, K::BMW, K::NT>(a, k.c);
         return;
     }
+    __syncthreads();  // every wave is done with the first block's LDS tiles
     if (PP)
         k.run_pp(a, logit_scale);
     else
@@ -1616,6 +1665,31 @@ dim3 grid_for(const RunArgs& a, int bm) {
     return dim3(static_cast<unsigned>(n_qblocks) * a.batch * a.n_heads);
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Pairs of query blocks (n-1-j, j) all cover the same number of key tiles, so
+// a paired launch balances exactly when its pairs fill whole rounds of one
+// workgroup per CU.  Taken when the last round is at least 7/8 full: then
+// nearly every CU would run two blocks of an unpaired launch back to back.
+bool use_pairs(const RunArgs& a) {
+    const long long n_qb = (a.seq_len + 255) / 256;
+    if (n_qb < 2) return false;
+    const long long cus = device_cus();
+    const long long pairs = (n_qb + 1) / 2 * a.batch * a.n_heads;
+    const long long last = pairs % cus;
+    return pairs >= cus * 7 / 8 && (last == 0 || last >= cus * 7 / 8);
+}
+
 // Workgroup shape from prefill_uses_eight_waves; a non-null index map selects
 // the cached-prefill instantiation, n_split > 1 (with the map) the split-K one.
 template <int D, bool M, bool SP>
@@ -1624,15 +1698,18 @@ void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
     if (prefill_uses_eight_waves(a)) {
         dim3 g = grid_for(a, 256);
         g.x *= ns;
-        // head_dim 128 plain prefill runs the two-group schedule (measured
-        // faster there; slower for 64 and 96, whose waves hold fewer registers).
+        RunArgs b = a;
+        if (!SP && use_pairs(a)) {
+            b.paired = 1;
+            g.x = static_cast<unsigned>(((a.seq_len + 255) / 256 + 1) / 2) * a.batch * a.n_heads;
+        }
         // head_dim 128 runs the two-group schedule (its single S buffer keeps
         // the kernel out of spills, cached and split launches included).
         // Split launches otherwise keep one barrier per tile: their short key
         // ranges would pay the deeper prologue of the paired schedule.
         constexpr bool kPP = D == 128;
         hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP, false, kPP, !kPP && !SP>), g,
-                           dim3(512), 0, s, a, a.score_scale * kLog2e);
+                           dim3(512), 0, s, b, a.score_scale * kLog2e);
     } else {
         dim3 g = grid_for(a, 128);
         g.x *= ns;

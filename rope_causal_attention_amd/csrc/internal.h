@@ -34,6 +34,10 @@ struct RunArgs {
     // rows = batch * seq_len * n_heads in the order of O.
     int n_split;
     float* ws;
+    // Paired launch (unsplit eight-wave kernels): workgroup (j, batch, head)
+    // runs query block n_qblocks - 1 - j and then block j, so every pair
+    // covers the same number of key tiles.
+    int paired;
 };
 
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t stream);

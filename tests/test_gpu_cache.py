@@ -142,6 +142,7 @@ PLAIN_CASES = [
     # name, B, Hq, Hkv, S, D, dtype, theta
     ("same_bf16_4wave", 1, 4, 2, 300, 128, "bf16", 1e4),
     ("same_bf16_8wave", 1, 64, 8, 1030, 96, "bf16", 1e4),
+    ("same_bf16_8wave_paired", 1, 64, 8, 2000, 96, "bf16", 1e4),  # 256 pairs of query blocks
     ("same_f32", 1, 2, 1, 200, 64, "f32", 1e4),
     ("same_i16", 1, 4, 4, 300, 128, "i16", 1e4),
 ]
@@ -217,6 +218,7 @@ def _chunked(attn, q, k, v, chunks, kv_map, n_slots, dt, scale):
     ("chunk_8wave_d128", 4, 32, 8, 128, [512, 512, 512]),
     ("chunk_8wave_d96", 2, 32, 32, 96, [1024, 1024]),  # paired-barrier schedule at head_dim 96
     ("chunk_8wave_odd_tiles", 4, 32, 8, 128, [320, 704]),  # prefix 320: an odd count of whole tiles
+    ("chunk_8wave_paired", 2, 64, 16, 96, [2048, 1024]),  # paired launches: two rounds, then one
     ("chunk_ragged_d64", 2, 8, 2, 64, [100, 333, 1, 250]),
 ])
 def test_chunked_prefill_equals_plain_prefill(name, B, Hq, Hkv, D, chunks):

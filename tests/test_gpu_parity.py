@@ -62,13 +62,21 @@ PINGPONG_CASES = [
     ("pp_d128_ragged", 2, 32, 32, 1030, 128, 1e6, None),
     ("pp_d64_exact", 1, 64, 8, 1024, 64, 1e4, [5]),
     ("pp_d128_gqa4_offsets", 2, 32, 8, 1100, 128, 1e4, [0, 300]),  # two-group schedule, GQA 4, offsets
+    # Paired launches (224..256 pairs of query blocks on a 256-CU device): each
+    # workgroup runs block n-1-j, then block j of the same head.
+    ("paired_d96_odd_ragged", 1, 64, 16, 1700, 96, 1e4, [3]),  # 7 blocks: the middle one runs alone
+    ("paired_d128_last_block_8_rows", 2, 32, 8, 1800, 128, 1e6, [0, 77]),  # 8 blocks, the last holds 8 rows
+    ("paired_d64_exact", 1, 64, 64, 2048, 64, 1e4, None),
 ]
 
 
 @pytest.mark.parametrize("case", PINGPONG_CASES, ids=[c[0] for c in PINGPONG_CASES])
 def test_pingpong_shapes_full_compare(case):
     name, B, Hq, Hkv, S, D, theta, offs = case
-    assert B * Hq * ((S + 255) // 256) >= 256
+    n_qb = (S + 255) // 256
+    assert B * Hq * n_qb >= 256
+    if name.startswith("paired"):
+        assert 224 <= (n_qb + 1) // 2 * B * Hq <= 256
     announce(name)
     max_seq = S + (max(offs) if offs else 0)
     w = synth.Workload(name, B, Hq, Hkv, S, D, "bf16", theta, seed=sum(map(ord, name)), max_seq=max_seq)
