@@ -351,6 +351,7 @@ struct VStage {
 template <int D, int NT>
 struct Bf16QK {
     static constexpr int kStride = D + 8;  // f16 per K' row (16-byte pad against bank conflicts)
+    static constexpr bool kSerialBlocks = false;  // the two key blocks' MFMAs may interleave
     static constexpr int kBytes = BN * kStride * 2;
     static constexpr int kChunks = BN * D / 8;  // 16-byte chunks per K tile
     static constexpr int kPer = (kChunks + NT - 1) / NT;
@@ -469,6 +470,10 @@ struct Bf16QK {
 template <int D, int NT>
 struct I16QK {
     static constexpr int kRow = D + 16;  // bytes per 8-bit digit row
+    // The scores of the two 32-key blocks of a tile are formed one block at a
+    // time (three int32 accumulators each), which keeps the eight-wave kernels
+    // within their register budget.
+    static constexpr bool kSerialBlocks = true;
     static constexpr int kPlane = BN * kRow;
     static constexpr int kBytes = 3 * kPlane;  // planes: high digit, low digit, high + low
     static constexpr int kChunks = BN * D / 8;
@@ -960,6 +965,7 @@ struct FusedAttn {
     __device__ __forceinline__ void qk_tile(int t, float* s) const {
         const int na = FULL ? 2 : nact(t);
         if (na >= 1) P::qk(kbuf(t), 0, q, s, lq, lh);
+        if (P::kSerialBlocks) __builtin_amdgcn_sched_barrier(0);
         if (na == 2) P::qk(kbuf(t), 1, q, s + 16, lq, lh);
     }
 
@@ -1732,6 +1738,22 @@ hipError_t launch_bf16_d(const RunArgs& a, hipStream_t s) {
 }
 template <int D, template <int, int> class QKT>
 hipError_t launch_int_d(const RunArgs& a, hipStream_t s) {
+    // Plain head_dim 128 launches that fill the chip run the eight-wave
+    // two-group kernel (half the K staging and quantisation per query row); at
+    // 64 and 96 the int variants' extra Q digit planes push it into spills.
+    if constexpr (D == 128) {
+        if (!a.kv_map && prefill_uses_eight_waves(a)) {
+            dim3 g = grid_for(a, 256);
+            RunArgs b = a;
+            if (use_pairs(a)) {
+                b.paired = 1;
+                g.x = static_cast<unsigned>(((a.seq_len + 255) / 256 + 1) / 2) * a.batch * a.n_heads;
+            }
+            hipLaunchKernelGGL((attn_fwd_kernel<D, QKT, VStage8, 8, 1, false, false, false, true>), g, dim3(512), 0, s,
+                               b, a.score_scale * kLog2e);
+            return hipGetLastError();
+        }
+    }
     if (a.kv_map && a.n_split > 1) {
         dim3 g = grid_for(a, 128);
         g.x *= a.n_split;

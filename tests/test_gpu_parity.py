@@ -213,6 +213,32 @@ def test_int16_attention_output():
     assert mx <= 1e-2
 
 
+# Plain head_dim 128 launches with at least 256 workgroups of 256 query rows
+# run the int16 and in-kernel quantised variants on the eight-wave two-group
+# kernel.
+EIGHT_WAVE_INT = [
+    # name, B, Hq, Hkv, S, D, dtype, offsets
+    ("i16_8wave_d128_gqa_offsets", 2, 32, 8, 1100, 128, "i16", [0, 300]),
+    ("i16_8wave_d128_paired", 1, 64, 16, 1800, 128, "i16", None),  # 8 blocks, the last of 8 rows: 256 pairs
+    ("q16_8wave_d128_ragged", 1, 64, 8, 1030, 128, "bf16q", [7]),
+    ("q16_8wave_d128_paired_odd", 1, 64, 8, 1700, 128, "bf16q", None),  # 7 blocks: the middle one alone
+]
+
+
+@pytest.mark.parametrize("case", EIGHT_WAVE_INT, ids=[c[0] for c in EIGHT_WAVE_INT])
+def test_int_variants_eight_wave_full_compare(case):
+    name, B, Hq, Hkv, S, D, dt, offs = case
+    assert B * Hq * ((S + 255) // 256) >= 256
+    announce(name)
+    max_seq = S + (max(offs) if offs else 0)
+    scale = 2.0 ** -22 / np.sqrt(D) if dt == "i16" else 0.0
+    w = synth.Workload(name, B, Hq, Hkv, S, D, dt, 1e4, sum(map(ord, name)), score_scale=scale, max_seq=max_seq)
+    q, k, v = synth.make_inputs(w)
+    got = run_gpu(w, q, k, v, pos_offsets=offs)
+    mx, mean = assert_close(got.numpy(), oracle_full(w, q, k, v, pos_offsets=offs), "bf16")
+    announce(name, f"max {mx:.2e} mean {mean:.2e}")
+
+
 def test_int16_degenerate_scale_small():
     """A large score scale makes the softmax nearly one-hot: exercises ties and argmax."""
     w = synth.Workload("i16_sharp", 1, 2, 2, 130, 128, "i16", 1e4, 88, score_scale=2.0 ** -8 / 11.3137085)
