@@ -124,6 +124,16 @@ def cpu_baseline(w, budget_s):
 DECODE = dict(batch=16, ctx=4096, n_heads=32, n_kv_heads=8, head_dim=128, rope_theta=1e4, block=64, seed=2024)
 
 
+def calib_copy(torch):
+    """A plain 256 MiB elementwise copy: what the HBM byte counters read for known traffic."""
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_decode(args, torch, pa):
     """Decode attention over a paged bf16 cache; prints one JSON line."""
     import numpy as np
@@ -153,6 +163,8 @@ def bench_decode(args, torch, pa):
     torch.cuda.synchronize()
     if attn.status() != pa.PA_OK:
         raise RuntimeError("status word set during warm-up")
+    if args.calib_copy:
+        calib_copy(torch)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -253,12 +265,7 @@ def main():
         raise RuntimeError("status word set during warm-up")
 
     if args.calib_copy:
-        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")  # 256 MiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calib_copy(torch)
 
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
