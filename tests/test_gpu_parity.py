@@ -67,6 +67,10 @@ PINGPONG_CASES = [
     ("paired_d96_odd_ragged", 1, 64, 16, 1700, 96, 1e4, [3]),  # 7 blocks: the middle one runs alone
     ("paired_d128_last_block_8_rows", 2, 32, 8, 1800, 128, 1e6, [0, 77]),  # 8 blocks, the last holds 8 rows
     ("paired_d64_exact", 1, 64, 64, 2048, 64, 1e4, None),
+    # (batch, head) counts that are not a multiple of 8 take the plain
+    # round-robin order instead of per-XCD head ranges.
+    ("paired_bh60_gqa5_d64", 1, 60, 12, 2048, 64, 1e4, [11]),  # 240 pairs
+    ("pp_bh36_gqa3_d96", 1, 36, 12, 2000, 96, 1e4, None),  # 288 blocks, unpaired
 ]
 
 
