@@ -291,34 +291,48 @@ __global__ __launch_bounds__(kThreads, G >= 8 ? 2 : 4) void decode_kernel(Decode
 }
 
 // O = sum_s w_s O_s / sum_s w_s l_s with w_s = exp2(m_s - max m), in one
-// pass over the splits (running max, rescaled running sums), so the reads of
-// all splits are independent of each other.  One wave per (b, h); lane d
-// handles dims d and d + 64.
+// pass over the splits (running max, rescaled running sums).  The loads of
+// four splits are issued together before any of them is used; the O part of
+// an empty split (max = -inf) may be unwritten, so it is selected out rather
+// than weighted.  One wave per (b, h); lane d handles dims d and d + 64.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     constexpr int PER = (D + 63) / 64;
+    constexpr int CH = 4;  // splits whose loads are in flight together
     const size_t bh = blockIdx.x;
     const float* ml = a.ws + static_cast<size_t>(a.batch) * a.n_heads * a.n_split * D;
     float M = kNegInf, L = 0.f, O[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) O[i] = 0.f;
-#pragma unroll 4
-    for (int s = 0; s < a.n_split; ++s) {
-        const size_t part = bh * a.n_split + s;
-        const float2 st = *reinterpret_cast<const float2*>(ml + 2 * part);
-        if (st.x == kNegInf) continue;  // empty split: its O part is not read (may be unwritten)
-        float o[PER];
+    for (int s0 = 0; s0 < a.n_split; s0 += CH) {
+        float2 st[CH];
+        float o[CH][PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int d = threadIdx.x + 64 * i;
-            o[i] = d < D ? a.ws[part * D + d] : 0.f;
+        for (int c = 0; c < CH; ++c) {
+            const int s = s0 + c;
+            st[c] = make_float2(kNegInf, 0.f);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) o[c][i] = 0.f;
+            if (s < a.n_split) {
+                const size_t part = bh * a.n_split + s;
+                st[c] = *reinterpret_cast<const float2*>(ml + 2 * part);
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int d = threadIdx.x + 64 * i;
+                    if (d < D) o[c][i] = a.ws[part * D + d];
+                }
+            }
         }
-        const float M2 = fmaxf(M, st.x);
-        const float f_old = weight(M, M2), f_new = __builtin_amdgcn_exp2f(st.x - M2);
-        L = L * f_old + st.y * f_new;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) O[i] = O[i] * f_old + o[i] * f_new;
-        M = M2;
+        for (int c = 0; c < CH; ++c) {
+            if (st[c].x == kNegInf) continue;  // empty split (or past the last)
+            const float M2 = fmaxf(M, st[c].x);
+            const float f_old = weight(M, M2), f_new = __builtin_amdgcn_exp2f(st[c].x - M2);
+            L = L * f_old + st[c].y * f_new;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) O[i] = O[i] * f_old + o[c][i] * f_new;
+            M = M2;
+        }
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
