@@ -921,10 +921,17 @@ struct VStage8 : VStage<D, NT> {
 // barrier that follows its last read, and a tile is whole one barrier before
 // it is read.
 template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, bool MAPPED, bool SPLIT,
-          bool PWL = false, bool PP = false, bool PAIR = false>
+          bool PWL = false, bool PP = false, bool PAIR = false, int GP = 1>
 struct FusedAttn {
     static constexpr int NT = 64 * NW;
     static constexpr int BMW = 32 * NW;
+    // GP = 2 packs the two query heads of a KV-head pair into one workgroup:
+    // waves [0, NW/2) take the first head, the others the second, each wave
+    // the same 32 query positions in both halves, so a K/V tile staged once
+    // serves both heads and a block spans BMP = BMW / GP query positions.
+    static_assert(GP == 1 || (GP == 2 && NW == 8), "head packing needs eight waves");
+    static constexpr int BMP = BMW / GP;
+    static constexpr int WPH = NW / GP;  // waves per head
     using P = QKT<D, NT>;
     using V = VST<D, NT>;
     static_assert(!PP || (NW == 8 && !PWL), "the two-group schedule needs eight waves");
@@ -1185,9 +1192,9 @@ struct FusedAttn {
         const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
         lq = lane & 31;
         lh = lane >> 5;
-        qw0 = c.q0 + 32 * w;
+        qw0 = c.q0 + 32 * (w % WPH);
         kq0 = c.kshift + qw0;
-        const int n_all = (c.kshift + min(c.q0 + BMW, c.S) + BN - 1) / BN;
+        const int n_all = (c.kshift + min(c.q0 + BMP, c.S) + BN - 1) / BN;
         const int n_full = min((c.kshift + c.q0) / BN, n_all);
         t_lo = 0;
         n_tiles = n_all;
@@ -1302,9 +1309,9 @@ struct FusedAttn {
         const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
         lq = lane & 31;
         lh = lane >> 5;
-        qw0 = c.q0 + 32 * w;
+        qw0 = c.q0 + 32 * (w % WPH);
         kq0 = c.kshift + qw0;
-        const int n_all = (c.kshift + min(c.q0 + BMW, c.S) + BN - 1) / BN;
+        const int n_all = (c.kshift + min(c.q0 + BMP, c.S) + BN - 1) / BN;
         const int n_full = min((c.kshift + c.q0) / BN, n_all);  // tiles every query of the workgroup sees whole
         t_lo = 0;
         n_tiles = n_all;
@@ -1391,9 +1398,9 @@ struct FusedAttn {
 };
 
 template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, int MINB, bool MAPPED,
-          bool SPLIT = false, bool PWL = false, bool PP = false, bool PAIR = false>
+          bool SPLIT = false, bool PWL = false, bool PP = false, bool PAIR = false, int GP = 1>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, float logit_scale) {
-    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT, PWL, PP, PAIR>;
+    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT, PWL, PP, PAIR, GP>;
     __shared__ __attribute__((aligned(16))) char lds[K::kLds];
     __shared__ float knots[PWL ? 9 : 1];
     K k;
@@ -1407,31 +1414,50 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, floa
         knots[threadIdx.x] = kE[threadIdx.x];
     }
     // One query block, or two in a paired launch (eight-wave kernels only).
+    // With head packing, blocks are enumerated over (batch, head pair) and
+    // each wave then moves to its own head of the pair.
     const bool paired = !SPLIT && NW == 8 && a.paired;
-    const int n_qblocks = (a.seq_len + K::BMW - 1) / K::BMW;
+    const int n_qblocks = (a.seq_len + K::BMP - 1) / K::BMP;
     const int bid = SPLIT ? static_cast<int>(blockIdx.x) / a.n_split : static_cast<int>(blockIdx.x);
     const int split = SPLIT ? static_cast<int>(blockIdx.x) % a.n_split : 0;
-    const BlockPos bp = paired ? map_pair(n_qblocks, a.batch, a.n_heads, bid, 0)
-                               : map_block(n_qblocks, a.batch, a.n_heads, bid);
-    const bool ok = make_ctx_at<K::BMW, MAPPED>(a, bp, split, k.c);
+    const int hw = GP > 1 ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) / K::WPH : 0;
+    auto block = [&](int item) {
+        BlockPos bp = paired ? map_pair(n_qblocks, a.batch, a.n_heads / GP, bid, item)
+                             : map_block(n_qblocks, a.batch, a.n_heads / GP, bid);
+        bp.hq *= GP;
+        return bp;
+    };
+    // A sequence whose positions leave the tables: every head of the block gets O = 0.
+    auto zero_block = [&]() {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            Ctx cz = k.c;
+            cz.hq += h;
+            if (SPLIT)
+                zero_partials<D, K::BMP, K::NT>(a, cz);
+            else
+                zero_rows<D, K::BMP, K::NT>(a, cz);
+        }
+    };
+    const BlockPos bp = block(0);
+    const bool ok = make_ctx_at<K::BMP, MAPPED>(a, bp, split, k.c);
     if (!ok) {
-        if (SPLIT)
-            zero_partials<D, K::BMW, K::NT>(a, k.c);
-        else
-            zero_rows<D, K::BMW, K::NT>(a, k.c);
-    } else if (PP) {
-        k.run_pp(a, logit_scale);
+        zero_block();
     } else {
-        k.run(a, logit_scale);
+        k.c.hq += hw;
+        if (PP)
+            k.run_pp(a, logit_scale);
+        else
+            k.run(a, logit_scale);
     }
     if (!paired || 2 * bp.qb == n_qblocks - 1) return;  // the middle block of an odd count runs alone
     // Second block of the pair: same (batch, head), so the same validity.
-    const BlockPos bp2 = map_pair(n_qblocks, a.batch, a.n_heads, bid, 1);
-    make_ctx_at<K::BMW, MAPPED>(a, bp2, split, k.c);
+    make_ctx_at<K::BMP, MAPPED>(a, block(1), split, k.c);
     if (!ok) {
-        zero_rows<D, K::BMW, K::NT>(a, k.c);
+        zero_block();
         return;
     }
+    k.c.hq += hw;
     __syncthreads();  // every wave is done with the first block's LDS tiles
     if (PP)
         k.run_pp(a, logit_scale);
@@ -1687,11 +1713,11 @@ int device_cus() {
 // a paired launch balances exactly when its pairs fill whole rounds of one
 // workgroup per CU.  Taken when the last round is at least 7/8 full: then
 // nearly every CU would run two blocks of an unpaired launch back to back.
-bool use_pairs(const RunArgs& a) {
-    const long long n_qb = (a.seq_len + 255) / 256;
+bool use_pairs(const RunArgs& a, int rows = 256, int head_pack = 1) {
+    const long long n_qb = (a.seq_len + rows - 1) / rows;
     if (n_qb < 2) return false;
     const long long cus = device_cus();
-    const long long pairs = (n_qb + 1) / 2 * a.batch * a.n_heads;
+    const long long pairs = (n_qb + 1) / 2 * a.batch * (a.n_heads / head_pack);
     const long long last = pairs % cus;
     return pairs >= cus * 7 / 8 && (last == 0 || last >= cus * 7 / 8);
 }
@@ -1701,6 +1727,21 @@ bool use_pairs(const RunArgs& a) {
 template <int D, bool M, bool SP>
 void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
     const int ns = SP ? a.n_split : 1;
+    // Plain launches whose query heads come in pairs per KV head pack both
+    // heads of a pair into one workgroup of 128 query positions.
+    if (!M && !SP && prefill_uses_eight_waves(a) && (a.n_heads / a.n_kv_heads) % 2 == 0) {
+        const unsigned n_qb = static_cast<unsigned>((a.seq_len + 127) / 128);
+        dim3 g(n_qb * a.batch * (a.n_heads / 2));
+        RunArgs b = a;
+        if (use_pairs(a, 128, 2)) {
+            b.paired = 1;
+            g.x = (n_qb + 1) / 2 * a.batch * (a.n_heads / 2);
+        }
+        constexpr bool kPP = D == 128;
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, false, false, false, kPP, !kPP, 2>), g,
+                           dim3(512), 0, s, b, a.score_scale * kLog2e);
+        return;
+    }
     if (prefill_uses_eight_waves(a)) {
         dim3 g = grid_for(a, 256);
         g.x *= ns;
