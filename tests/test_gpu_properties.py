@@ -107,6 +107,54 @@ def test_out_of_range_offsets_zero_the_element_and_report():
         attn.close()
 
 
+# Eight-wave launches: plain order, paired blocks, and GQA head packing
+# (two query heads of a KV head per workgroup), paired and not.
+EIGHT_WAVE = [
+    # name, Hq, Hkv
+    ("pack_unpaired", 32, 16),
+    ("pack_paired", 64, 32),
+    ("mha_paired", 64, 64),
+]
+
+
+@pytest.mark.parametrize("name,Hq,Hkv", EIGHT_WAVE, ids=[c[0] for c in EIGHT_WAVE])
+def test_out_of_range_offsets_eight_wave(name, Hq, Hkv):
+    """Element 1's positions leave the table: every head of it is zero, the
+    status is reported, and element 0 equals its own single-element run."""
+    announce("erange8", name)
+    B, S, D, max_seq = 2, 1024, 64, 1100
+    assert B * Hq * (S // 256) >= 256
+    w = synth.Workload(name, B, Hq, Hkv, S, D, "bf16", 1e4, sum(map(ord, name)), max_seq=max_seq)
+    q, k, v = synth.make_inputs(w)
+    attn = pa.PrefillAttention(Hq, Hkv, D, max_seq, 1e4)
+    try:
+        qd, kd, vd = to_dev(q, k, v)
+        out = torch.full(q.shape, 7.0, dtype=torch.float32, device="cuda")
+        off = torch.tensor([50, 77], dtype=torch.int32, device="cuda")  # 77 + 1024 > 1100
+        attn(qd, kd, vd, pos_offsets=off, out=out)
+        assert attn.status() == pa.PA_ERANGE
+        o = out.cpu()
+        assert torch.all(o[1] == 0)
+        o0 = attn(qd[:1].contiguous(), kd[:1].contiguous(), vd[:1].contiguous(),
+                  pos_offsets=torch.tensor([50], dtype=torch.int32, device="cuda")).cpu()
+        assert attn.status() == pa.PA_OK
+        assert torch.equal(o[:1], o0)
+    finally:
+        attn.close()
+
+
+def test_gqa_head_packing_equals_mha_with_repeated_kv_bitwise():
+    """Two query heads per KV head on the eight-wave kernel (packed) against
+    the same attention with K/V repeated per query head (unpacked)."""
+    announce("gqa8")
+    w = synth.Workload("gqa8", 1, 32, 16, 2048, 64, "bf16", 1e4, 4242)
+    q, k, v = synth.make_inputs(w)
+    o = run_gpu(w, q, k, v)
+    w2 = synth.Workload("gqa8", 1, 32, 32, 2048, 64, "bf16", 1e4, 4242)
+    o2 = run_gpu(w2, q, k.repeat_interleave(2, dim=2).contiguous(), v.repeat_interleave(2, dim=2).contiguous())
+    assert torch.equal(o, o2)
+
+
 def test_empty_inputs_are_noops():
     attn = pa.PrefillAttention(2, 2, 64, 16, 1e4)
     try:
