@@ -1727,9 +1727,9 @@ bool use_pairs(const RunArgs& a, int rows = 256, int head_pack = 1) {
 template <int D, bool M, bool SP>
 void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
     const int ns = SP ? a.n_split : 1;
-    // Plain launches whose query heads come in pairs per KV head pack both
+    // Unsplit launches whose query heads come in pairs per KV head pack both
     // heads of a pair into one workgroup of 128 query positions.
-    if (!M && !SP && prefill_uses_eight_waves(a) && (a.n_heads / a.n_kv_heads) % 2 == 0) {
+    if (!SP && prefill_uses_eight_waves(a) && (a.n_heads / a.n_kv_heads) % 2 == 0) {
         const unsigned n_qb = static_cast<unsigned>((a.seq_len + 127) / 128);
         dim3 g(n_qb * a.batch * (a.n_heads / 2));
         RunArgs b = a;
@@ -1738,7 +1738,7 @@ void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
             g.x = (n_qb + 1) / 2 * a.batch * (a.n_heads / 2);
         }
         constexpr bool kPP = D == 128;
-        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, false, false, false, kPP, !kPP, 2>), g,
+        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, false, false, kPP, !kPP, 2>), g,
                            dim3(512), 0, s, b, a.score_scale * kLog2e);
         return;
     }
