@@ -925,11 +925,11 @@ template <int D, template <int, int> class QKT, template <int, int> class VST, i
 struct FusedAttn {
     static constexpr int NT = 64 * NW;
     static constexpr int BMW = 32 * NW;
-    // GP = 2 packs the two query heads of a KV-head pair into one workgroup:
-    // waves [0, NW/2) take the first head, the others the second, each wave
-    // the same 32 query positions in both halves, so a K/V tile staged once
-    // serves both heads and a block spans BMP = BMW / GP query positions.
-    static_assert(GP == 1 || (GP == 2 && NW == 8), "head packing needs eight waves");
+    // GP > 1 packs GP query heads that share a KV head into one workgroup:
+    // waves [g NW/GP, (g+1) NW/GP) take head g of the pack, each group of
+    // waves the same query positions, so a K/V tile staged once serves all GP
+    // heads and a block spans BMP = BMW / GP query positions.
+    static_assert(GP == 1 || ((GP == 2 || GP == 4) && NW == 8), "head packing needs eight waves");
     static constexpr int BMP = BMW / GP;
     static constexpr int WPH = NW / GP;  // waves per head
     using P = QKT<D, NT>;
@@ -1727,19 +1727,25 @@ bool use_pairs(const RunArgs& a, int rows = 256, int head_pack = 1) {
 template <int D, bool M, bool SP>
 void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
     const int ns = SP ? a.n_split : 1;
-    // Unsplit launches whose query heads come in pairs per KV head pack both
-    // heads of a pair into one workgroup of 128 query positions.
-    if (!SP && prefill_uses_eight_waves(a) && (a.n_heads / a.n_kv_heads) % 2 == 0) {
-        const unsigned n_qb = static_cast<unsigned>((a.seq_len + 127) / 128);
-        dim3 g(n_qb * a.batch * (a.n_heads / 2));
+    // Unsplit launches whose query heads share KV heads in groups of 4 (or 2)
+    // pack 4 (2) heads of a group into one workgroup of 64 (128) query positions.
+    const int group = a.n_heads / a.n_kv_heads;
+    if (!SP && prefill_uses_eight_waves(a) && group % 2 == 0) {
+        const int gp = group % 4 == 0 ? 4 : 2, rows = 256 / gp;
+        const unsigned n_qb = static_cast<unsigned>((a.seq_len + rows - 1) / rows);
+        dim3 g(n_qb * a.batch * (a.n_heads / gp));
         RunArgs b = a;
-        if (use_pairs(a, 128, 2)) {
+        if (use_pairs(a, rows, gp)) {
             b.paired = 1;
-            g.x = (n_qb + 1) / 2 * a.batch * (a.n_heads / 2);
+            g.x = (n_qb + 1) / 2 * a.batch * (a.n_heads / gp);
         }
         constexpr bool kPP = D == 128;
-        hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, false, false, kPP, !kPP, 2>), g,
-                           dim3(512), 0, s, b, a.score_scale * kLog2e);
+        if (gp == 4)
+            hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, false, false, kPP, !kPP, 4>), g,
+                               dim3(512), 0, s, b, a.score_scale * kLog2e);
+        else
+            hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, false, false, kPP, !kPP, 2>), g,
+                               dim3(512), 0, s, b, a.score_scale * kLog2e);
         return;
     }
     if (prefill_uses_eight_waves(a)) {
