@@ -1727,24 +1727,24 @@ bool use_pairs(const RunArgs& a, int rows = 256, int head_pack = 1) {
 template <int D, bool M, bool SP>
 void launch_bf16_dm(const RunArgs& a, hipStream_t s) {
     const int ns = SP ? a.n_split : 1;
-    // Unsplit launches whose query heads share KV heads in groups of 4 (or 2)
-    // pack 4 (2) heads of a group into one workgroup of 64 (128) query positions.
+    // Launches whose query heads share KV heads in groups of 4 (or 2) pack 4
+    // (2) heads of a group into one workgroup of 64 (128) query positions.
     const int group = a.n_heads / a.n_kv_heads;
-    if (!SP && prefill_uses_eight_waves(a) && group % 2 == 0) {
+    if (prefill_uses_eight_waves(a) && group % 2 == 0) {
         const int gp = group % 4 == 0 ? 4 : 2, rows = 256 / gp;
         const unsigned n_qb = static_cast<unsigned>((a.seq_len + rows - 1) / rows);
-        dim3 g(n_qb * a.batch * (a.n_heads / gp));
+        dim3 g(n_qb * a.batch * (a.n_heads / gp) * ns);
         RunArgs b = a;
-        if (use_pairs(a, rows, gp)) {
+        if (!SP && use_pairs(a, rows, gp)) {
             b.paired = 1;
             g.x = (n_qb + 1) / 2 * a.batch * (a.n_heads / gp);
         }
         constexpr bool kPP = D == 128;
         if (gp == 4)
-            hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, false, false, kPP, !kPP, 4>), g,
+            hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP, false, kPP, !kPP && !SP, 4>), g,
                                dim3(512), 0, s, b, a.score_scale * kLog2e);
         else
-            hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, false, false, kPP, !kPP, 2>), g,
+            hipLaunchKernelGGL((attn_fwd_kernel<D, Bf16Stage8, VStage8, 8, 1, M, SP, false, kPP, !kPP && !SP, 2>), g,
                                dim3(512), 0, s, b, a.score_scale * kLog2e);
         return;
     }
