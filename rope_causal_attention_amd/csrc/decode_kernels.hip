@@ -341,6 +341,49 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     }
 }
 
+// The same merge for the many short rows of split-K prefill: each thread owns
+// 4 dims (16-byte loads and stores) of one row, a workgroup 256 / (D/4) rows.
+template <int D>
+__global__ __launch_bounds__(256) void split_merge_rows_kernel(DecodeArgs a) {
+    constexpr int C4 = D / 4;         // float4 per row
+    constexpr int RPB = 256 / C4;     // rows per workgroup
+    constexpr int CH = 4;             // splits whose loads are in flight together
+    const int r = static_cast<int>(threadIdx.x) / C4, c4 = static_cast<int>(threadIdx.x) % C4;
+    const size_t rows = static_cast<size_t>(a.batch) * a.n_heads;
+    const size_t row = static_cast<size_t>(blockIdx.x) * RPB + r;
+    if (r >= RPB || row >= rows) return;
+    const float* ml = a.ws + rows * a.n_split * D;
+    float M = kNegInf, L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < a.n_split; s0 += CH) {
+        float2 st[CH];
+        float4 o[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int sp = s0 + c;
+            st[c] = make_float2(kNegInf, 0.f);
+            o[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (sp < a.n_split) {
+                const size_t part = row * a.n_split + sp;
+                st[c] = *reinterpret_cast<const float2*>(ml + 2 * part);
+                o[c] = *reinterpret_cast<const float4*>(a.ws + part * D + 4 * c4);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (st[c].x == kNegInf) continue;  // empty split (its O part may be unwritten) or past the last
+            const float M2 = fmaxf(M, st[c].x);
+            const float f_old = weight(M, M2), f_new = __builtin_amdgcn_exp2f(st[c].x - M2);
+            L = L * f_old + st[c].y * f_new;
+            O = make_float4(O.x * f_old + o[c].x * f_new, O.y * f_old + o[c].y * f_new, O.z * f_old + o[c].z * f_new,
+                            O.w * f_old + o[c].w * f_new);
+            M = M2;
+        }
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    *reinterpret_cast<float4*>(a.out + row * D + 4 * c4) = make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
+}
+
 template <int D, int G, bool F32>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
     const long long blocks = static_cast<long long>(a.batch) * (a.n_heads / G) * a.n_split;
@@ -371,13 +414,15 @@ int decode_group(int n_heads, int n_kv_heads) {
 }
 
 hipError_t launch_split_merge(int head_dim, const DecodeArgs& a, hipStream_t s) {
-    const long long blocks = static_cast<long long>(a.batch) * a.n_heads;
+    const long long rows = static_cast<long long>(a.batch) * a.n_heads;
+    const int rpb = 256 / (head_dim / 4);
+    const long long blocks = (rows + rpb - 1) / rpb;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 g(static_cast<unsigned>(blocks));
     switch (head_dim) {
-        case 64: hipLaunchKernelGGL((decode_merge_kernel<64>), g, dim3(64), 0, s, a); break;
-        case 96: hipLaunchKernelGGL((decode_merge_kernel<96>), g, dim3(64), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((decode_merge_kernel<128>), g, dim3(64), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((split_merge_rows_kernel<64>), g, dim3(256), 0, s, a); break;
+        case 96: hipLaunchKernelGGL((split_merge_rows_kernel<96>), g, dim3(256), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((split_merge_rows_kernel<128>), g, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
