@@ -359,6 +359,10 @@ SPLIT_CASES = [
     ("sk_bf16_d64_many", 2, 4, 2, 64, "bf16", 1e4, [64, 5], 77, "paged", 1024, 9),
     ("sk_i16_d128", 1, 4, 2, 128, "i16", 1e4, [900], 128, "paged", 2048, 3),
     ("sk_bf16_d128_8wave", 1, 32, 8, 128, "bf16", 1e4, [1500], 256, "paged", 2048, 8),  # two-group split
+    # Rows (B * S * Hq) not a multiple of the merge's rows per workgroup
+    # (10 at head_dim 96, 8 at 128): the last merge workgroup is partial.
+    ("sk_bf16_d96_merge_tail", 1, 3, 1, 96, "bf16", 1e4, [1300], 37, "paged", 2048, 5),
+    ("sk_bf16_d128_merge_tail", 1, 5, 1, 128, "bf16", 1e4, [611], 45, "ring", 1024, 3),
 ]
 
 
