@@ -212,7 +212,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        log("bench.py measures one GPU only: this build has no multi-GPU path "
+        log("bench.py measures one GPU only: the library has no multi-GPU path "
             "(heads or sequence shards would each run this kernel at their own shape). Use --gpus 1.")
         sys.exit(2)
 
