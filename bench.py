@@ -56,7 +56,7 @@ def algorithmic_bytes(w):
     q = w.batch * w.seq_len * w.n_heads * w.head_dim * el
     kv = 2 * w.batch * w.seq_len * w.n_kv_heads * w.head_dim * (el if w.dtype != "i16" else 2)
     o = w.batch * w.seq_len * w.n_heads * w.head_dim * 4
-    tab = w.seq_len * w.head_dim * (2 if w.dtype in ("i16", "bf16q") else 4)  # Q1.14 or fp32 pairs
+    tab = w.seq_len * w.head_dim * (4 if w.dtype == "f32" else 2)  # fp32, or fp16 / Q1.14 pairs
     return q + kv + o + tab
 
 

@@ -80,19 +80,25 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-// Rotated pair (x c - y s, x s + y c) packed as two fp16.  The products y s
-// and y c are rounded to fp32; each fused multiply-add then rounds once,
-// straight to fp16 (v_fma_mix with fp32 sources).  Spelled out so that every
-// copy of the staging code rounds K' the same way: left to itself the
-// compiler fuses the fp16 conversion into the FMA in some copies and not in
-// others, which would make K' depend on which pipeline step staged the tile.
-__device__ __forceinline__ uint32_t rot_pack_h2(float x, float y, float c, float s) {
-    const float ys = -y * s, yc = y * c;
+// Rotated pair (x c - y s, x s + y c) packed as two fp16, with the table's
+// fp16 (cos, sin) pair in one word (cos in the low half).  v_fma_mix takes the
+// fp16 halves as sources directly: the products y s and y c are formed and
+// rounded in fp32, and each fused multiply-add then rounds once, straight to
+// fp16.  Spelled out so that every copy of the staging code rounds K' the
+// same way: left to itself the compiler fuses the fp16 conversion into the
+// FMA in some copies and not in others, which would make K' depend on which
+// pipeline step staged the tile.
+__device__ __forceinline__ uint32_t rot_pack_h2h(float x, float y, uint32_t cs) {
+    float ys, yc;
+    asm("v_fma_mix_f32 %0, -%1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(ys) : "v"(y), "v"(cs));
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(yc) : "v"(y), "v"(cs));
     uint32_t r;
-    asm("v_fma_mixlo_f16 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(c), "v"(ys));
-    asm("v_fma_mixhi_f16 %0, %1, %2, %3" : "+v"(r) : "v"(x), "v"(s), "v"(yc));
+    asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(cs), "v"(ys));
+    asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(x), "v"(cs), "v"(yc));
     return r;
 }
+__device__ __forceinline__ float h_lo(uint32_t w) { return static_cast<float>(__builtin_bit_cast(f16x2, w)[0]); }
+__device__ __forceinline__ float h_hi(uint32_t w) { return static_cast<float>(__builtin_bit_cast(f16x2, w)[1]); }
 
 // Combine a per-lane value with the same lane of the other 32-lane half.
 __device__ __forceinline__ float halves_max(float x) {
@@ -360,24 +366,23 @@ struct Bf16QK {
     };
     struct KRegs {
         uint4 raw[kPer];
-        float4 c0[kPer], c1[kPer];
+        uint4 cs[kPer];  // fp16 (cos, sin) of the chunk's 4 pairs
     };
     struct KPtr {
         Rows k;
-        const char* tab;  // table row of position off[b]
+        const char* tab;  // fp16 table row of position off[b] (2 D bytes per position)
         int S;
     };
 
     // Rotate 4 adjacent pairs: x' = x c - y s, y' = x s + y c; times `scale`.
-    __device__ static __forceinline__ uint4 rotate8(const uint4& raw, const float4& c0, const float4& c1,
-                                                    float scale) {
+    __device__ static __forceinline__ uint4 rotate8(const uint4& raw, const uint4& cs, float scale) {
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-        const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const uint32_t t[4] = {cs.x, cs.y, cs.z, cs.w};
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float x = bf_lo(w[j]), y = bf_hi(w[j]);
-            const float c = cs[2 * j], s = cs[2 * j + 1];
+            const float c = h_lo(t[j]), s = h_hi(t[j]);
             const float xr = fmaf(x, c, -y * s), yr = fmaf(x, s, y * c);
             o[j] = pack_h2(xr * scale, yr * scale);
         }
@@ -387,25 +392,23 @@ struct Bf16QK {
     template <bool MAPPED>
     __device__ static __forceinline__ KPtr kptr(const RunArgs& a, const Ctx& c) {
         return {kv_rows<MAPPED>(a, c, a.k, D, 2),
-                reinterpret_cast<const char*>(a.rope_f32 + static_cast<size_t>(c.koff) * D), c.NK};
+                reinterpret_cast<const char*>(a.rope_h2 + static_cast<size_t>(c.koff) * (D / 2)), c.NK};
     }
 
     __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
         const int lh = (threadIdx.x & 63) >> 5;
         const bool ok = qi < c.S;
         const Rows rq = q_rows(a, c, a.q, D, 2);
-        const char* tab = reinterpret_cast<const char*>(a.rope_f32 + static_cast<size_t>(c.off) * D);
+        const char* tab = reinterpret_cast<const char*>(a.rope_h2 + static_cast<size_t>(c.off) * (D / 2));
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             const int d0 = 16 * ks + 8 * lh;
-            uint4 raw = make_uint4(0, 0, 0, 0);
-            float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0;
+            uint4 raw = make_uint4(0, 0, 0, 0), cs = raw;
             if (ok) {
                 raw = ld16(rq.base, qi * rq.stride + 2 * d0);
-                c0 = ld16f(tab, (qi * D + d0) * 4);
-                c1 = ld16f(tab, (qi * D + d0 + 4) * 4);
+                cs = ld16(tab, (qi * D + d0) * 2);
             }
-            q.f[ks] = __builtin_bit_cast(f16x8, rotate8(raw, c0, c1, scale));
+            q.f[ks] = __builtin_bit_cast(f16x8, rotate8(raw, cs, scale));
         }
     }
 
@@ -415,7 +418,7 @@ struct Bf16QK {
     template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
         const char* kb = p.k.template tile_base<MAPPED>(tile);
-        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
+        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int idx = min(static_cast<int>(threadIdx.x % NT) + NT * i, kChunks - 1);
@@ -423,18 +426,17 @@ struct Bf16QK {
             const int ch = idx % (D / 8);
             if (CLAMP) row = min(row, p.S - 1 - tile * BN);
             r.raw[i] = ld16(kb, p.k.template row_off<MAPPED>(tile, row) + 16 * ch);
-            r.c0[i] = ld16f(tb, (row * D + 8 * ch) * 4);
-            r.c1[i] = ld16f(tb, (row * D + 8 * ch + 4) * 4);
+            r.cs[i] = ld16(tb, (row * D + 8 * ch) * 2);
         }
     }
 
-    // K' = RoPE(K) rounded once to fp16 (rot_pack_h2).
-    __device__ static __forceinline__ uint4 rotate8_k(const uint4& raw, const float4& c0, const float4& c1) {
+    // K' = RoPE(K) rounded once to fp16 (rot_pack_h2h).
+    __device__ static __forceinline__ uint4 rotate8_k(const uint4& raw, const uint4& cs) {
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-        const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const uint32_t t[4] = {cs.x, cs.y, cs.z, cs.w};
         uint32_t o[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = rot_pack_h2(bf_lo(w[j]), bf_hi(w[j]), cs[2 * j], cs[2 * j + 1]);
+        for (int j = 0; j < 4; ++j) o[j] = rot_pack_h2h(bf_lo(w[j]), bf_hi(w[j]), t[j]);
         return make_uint4(o[0], o[1], o[2], o[3]);
     }
 
@@ -445,7 +447,7 @@ struct Bf16QK {
             if (!has(i)) continue;
             const int idx = static_cast<int>(threadIdx.x % NT) + NT * i;
             const int row = idx / (D / 8), ch = idx % (D / 8);
-            *reinterpret_cast<uint4*>(kl + row * kStride + 8 * ch) = rotate8_k(r.raw[i], r.c0[i], r.c1[i]);
+            *reinterpret_cast<uint4*>(kl + row * kStride + 8 * ch) = rotate8_k(r.raw[i], r.cs[i]);
         }
     }
 
@@ -822,7 +824,7 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
     static constexpr int kGran = D / 32;  // granules of 4 elements per thread
     struct KRegs {
         uint2 raw[kGran];
-        float4 cs[kGran];
+        uint2 cs[kGran];  // fp16 (cos, sin) of the granule's 2 pairs
     };
     template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
@@ -832,11 +834,11 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
         if (CLAMP) row = min(row, p.S - 1 - tile * BN);
         const char* kb = p.k.template tile_base<MAPPED>(tile);
         const uint32_t ro = p.k.template row_off<MAPPED>(tile, row);
-        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
+        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
 #pragma unroll
         for (int i = 0; i < kGran; ++i) {
             r.raw[i] = *reinterpret_cast<const uint2*>(kb + ro + 2 * (e0 + 4 * i));
-            r.cs[i] = ld16f(tb, (row * D + e0 + 4 * i) * 4);
+            r.cs[i] = *reinterpret_cast<const uint2*>(tb + (row * D + e0 + 4 * i) * 2);
         }
     }
     __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
@@ -847,10 +849,10 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
 #pragma unroll
         for (int i = 0; i < kGran; ++i) {
             const uint32_t w[2] = {r.raw[i].x, r.raw[i].y};
-            const float cs[4] = {r.cs[i].x, r.cs[i].y, r.cs[i].z, r.cs[i].w};
+            const uint32_t t[2] = {r.cs[i].x, r.cs[i].y};
             uint32_t o[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) o[j] = rot_pack_h2(bf_lo(w[j]), bf_hi(w[j]), cs[2 * j], cs[2 * j + 1]);
+            for (int j = 0; j < 2; ++j) o[j] = rot_pack_h2h(bf_lo(w[j]), bf_hi(w[j]), t[j]);
             *reinterpret_cast<uint2*>(kl + 4 * i) = make_uint2(o[0], o[1]);
         }
     }

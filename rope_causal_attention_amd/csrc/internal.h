@@ -15,6 +15,7 @@ struct RunArgs {
     float* out;
     const float* rope_f32;       // [max_seq][head_dim/2] (cos, sin) fp32 pairs
     const int16_t* rope_q14;     // [max_seq][head_dim/2] (C, S) Q1.14 pairs
+    const uint32_t* rope_h2;     // [max_seq][head_dim/2] (cos, sin) fp16 pairs, cos in the low half
     int* status;                 // set non-zero when a position leaves the table
     int batch;
     int seq_len;

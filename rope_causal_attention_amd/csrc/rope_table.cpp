@@ -5,8 +5,10 @@
 // theta_k, read as aligned pairs); the 2kiu.com retelling (§3.3, §4.2) builds
 // the table offline at high precision and rounds once to fixed point.  Here the
 // angle p*theta_k and its cos/sin are evaluated in fp64 on the host, then
-// rounded once: to fp32 (cos, sin) pairs for the float kernels and to Q1.14
-// int16 (C, S) pairs for the fixed-point kernel.  Interleaving cos and sin of
+// rounded once: to fp32 (cos, sin) pairs for the fp32 kernels and decode, to
+// fp16 pairs for the bf16 prefill kernels (whose rotated Q' and K' are fp16
+// anyway: half the table bytes per staged key), and to Q1.14 int16 (C, S)
+// pairs for the fixed-point kernel.  Interleaving cos and sin of
 // one pair lets a kernel fetch both with a single aligned load.
 
 #include <cmath>
@@ -42,6 +44,23 @@ extern "C" int prefill_attn_rope_table_f32(int max_seq, int head_dim, double rop
             const double a = static_cast<double>(p) * inv[k];
             row[2 * k + 0] = static_cast<float>(std::cos(a));
             row[2 * k + 1] = static_cast<float>(std::sin(a));
+        }
+    }
+    return PA_OK;
+}
+
+extern "C" int prefill_attn_rope_table_f16(int max_seq, int head_dim, double rope_theta, uint16_t* out) {
+    if (!table_args_ok(max_seq, head_dim, rope_theta, out)) return PA_EINVAL;
+    const int half = head_dim / 2;
+    const std::vector<double> inv = inverse_frequencies(head_dim, rope_theta);
+    for (int p = 0; p < max_seq; ++p) {
+        uint16_t* row = out + static_cast<size_t>(p) * head_dim;
+        for (int k = 0; k < half; ++k) {
+            const double a = static_cast<double>(p) * inv[k];
+            // fp64 -> fp16 in one rounding (nearest even)
+            const _Float16 c = static_cast<_Float16>(std::cos(a)), s = static_cast<_Float16>(std::sin(a));
+            row[2 * k + 0] = __builtin_bit_cast(uint16_t, c);
+            row[2 * k + 1] = __builtin_bit_cast(uint16_t, s);
         }
     }
     return PA_OK;
