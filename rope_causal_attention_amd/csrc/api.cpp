@@ -96,9 +96,7 @@ extern "C" int prefill_attn_init(prefill_attn** out, int n_heads, int n_kv_heads
     } catch (const std::bad_alloc&) {
         return PA_ENOMEM;
     }
-    if (prefill_attn_rope_table_f32(max_seq, head_dim, rope_theta, t32.data()) != PA_OK ||
-        prefill_attn_rope_table_q14(max_seq, head_dim, rope_theta, t14.data()) != PA_OK ||
-        prefill_attn_rope_table_f16(max_seq, head_dim, rope_theta, th.data()) != PA_OK)
+    if (pa::build_rope_tables(max_seq, head_dim, rope_theta, t32.data(), th.data(), t14.data()) != PA_OK)
         return PA_EINVAL;
 
     prefill_attn* h = new (std::nothrow) prefill_attn{dev, n_heads, n_kv_heads, head_dim, max_seq, rope_theta,

@@ -92,4 +92,8 @@ hipError_t launch_debug_rope_i16(int head_dim, const RunArgs& a, int n_heads_x, 
 hipError_t launch_debug_scores_i32(int head_dim, const RunArgs& a, int32_t* dst, hipStream_t stream);
 hipError_t launch_debug_scores_q16(int head_dim, const RunArgs& a, int32_t* dst, hipStream_t stream);
 
+// Host: the fp32, fp16 and Q1.14 RoPE tables of init from one fp64 pass
+// (each value rounded once, as the exported single-table builders do).
+int build_rope_tables(int max_seq, int head_dim, double rope_theta, float* f32, uint16_t* f16, int16_t* q14);
+
 }  // namespace pa
