@@ -42,6 +42,10 @@ struct RunArgs {
 };
 
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t stream);
+// bf16 prefill with K, V and table rows DMA'd into LDS (plain, unsplit launches
+// of eight-wave workgroups at head_dim 64 and 96).
+bool prefill_lds_supported(int head_dim, const RunArgs& a);
+hipError_t launch_prefill_lds(int head_dim, const RunArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t stream);
 hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t stream);
 // bf16 Q/K quantised in-kernel per (token, head) row to int16, then the int16 path.
@@ -78,6 +82,11 @@ struct DecodeArgs {
 // Merge of split-K partials: out[r][:] = sum_s w_s O_s / sum_s w_s l_s over the
 // rows r < a.batch * a.n_heads (DecodeArgs.batch counts row groups of n_heads).
 hipError_t launch_split_merge(int head_dim, const DecodeArgs& a, hipStream_t stream);
+// Compute units of the current device (cached per device).
+int device_cus();
+// Whether an eight-wave launch of `rows`-row query blocks (head_pack query
+// heads per workgroup) runs as pairs of blocks (n-1-j, j).
+bool use_pairs(const RunArgs& a, int rows = 256, int head_pack = 1);
 // Whether a cached-prefill launch of this shape uses eight-wave workgroups.
 bool prefill_uses_eight_waves(const RunArgs& a);
 
