@@ -73,8 +73,10 @@ enum prefill_attn_status {
     PA_ENOMEM = -2,  /* device or host allocation failed (init only) */
     PA_EDEVICE = -3, /* no device, or the current device is not gfx950 */
     PA_ELAUNCH = -4, /* the HIP runtime rejected a launch or a copy */
-    PA_ERANGE = -5   /* a run saw pos_offsets[b] < 0 or pos_offsets[b] + seq_len > max_seq (or, for the
+    PA_ERANGE = -5,  /* a run saw pos_offsets[b] < 0 or pos_offsets[b] + seq_len > max_seq (or, for the
                         cache calls, beyond map_stride, or a map entry outside the cache) */
+    PA_ETOOBIG = -6  /* prefill_attn_decode_noalloc: the requested split's partials exceed the
+                        library's fixed scratch */
 };
 
 /*
@@ -216,6 +218,32 @@ int prefill_attn_decode(const prefill_attn* h, int in_dtype, int batch, const vo
                         const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
                         float* out, float score_scale, int n_split,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * prefill_attn_decode_noalloc: prefill_attn_decode for callers that cannot
+ * allocate device memory or pass a workspace -- code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The split partials go
+ * to a scratch array that the library holds in device memory, one copy per
+ * device, from the first call on that device (init looks it up for the
+ * current device) until the process ends.  The call allocates nothing, also
+ * not through a library.
+ *
+ * Arguments, results, status and errors are prefill_attn_decode's, less the
+ * workspace.  The scratch holds prefill_attn_decode_noalloc_scratch_bytes()
+ * bytes (8 MiB): n_split = 0 chooses the split as prefill_attn_decode does and
+ * lowers it to what fits (down to 1, which uses no scratch); an explicit
+ * n_split > 1 whose partials, prefill_attn_decode_workspace_size(h, batch,
+ * n_split) bytes, exceed the scratch returns PA_ETOOBIG and enqueues nothing.
+ * The scratch needs no clearing (each split writes its partial before the merge
+ * reads it), but all calls on one device share it: two calls that may run at
+ * the same time on that device (other streams, other threads) race and give
+ * wrong results.  Calls on one stream are ordered and safe.
+ */
+int prefill_attn_decode_noalloc(const prefill_attn* h, int in_dtype, int batch, const void* q,
+                                const void* k_cache, const void* v_cache, int n_slots,
+                                const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
+                                float* out, float score_scale, int n_split, void* stream);
+size_t prefill_attn_decode_noalloc_scratch_bytes(void);
 
 /*
  * Host-only index-map builders (caller-owned host arrays; copy the result to the

@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "PA_IN_F32", "PA_IN_BF16", "PA_IN_I16", "PA_IN_BF16_Q16", "PA_IN_I16_PWL",
-    "PA_OK", "PA_EINVAL", "PA_ENOMEM", "PA_EDEVICE", "PA_ELAUNCH", "PA_ERANGE",
+    "PA_OK", "PA_EINVAL", "PA_ENOMEM", "PA_EDEVICE", "PA_ELAUNCH", "PA_ERANGE", "PA_ETOOBIG",
     "PrefillAttnError", "load_library", "library_path",
     "prefill_attn_init", "prefill_attn_run", "prefill_attn_status", "prefill_attn_destroy",
     "prefill_attn_strerror", "prefill_attn_rope_table_f32", "prefill_attn_rope_table_q14",
@@ -27,12 +27,13 @@ __all__ = [
     "prefill_attn_debug_rope_i16", "prefill_attn_debug_scores_i32", "prefill_attn_debug_scores_q16",
     "prefill_attn_kv_cache_update", "prefill_attn_run_cached", "prefill_attn_ring_map", "prefill_attn_paged_map",
     "prefill_attn_decode", "prefill_attn_decode_workspace_size",
+    "prefill_attn_decode_noalloc", "prefill_attn_decode_noalloc_scratch_bytes",
     "prefill_attn_run_cached_splitk", "prefill_attn_run_cached_workspace_size",
     "PrefillAttention", "EXPORTED_SYMBOLS",
 ]
 
 PA_IN_F32, PA_IN_BF16, PA_IN_I16, PA_IN_BF16_Q16, PA_IN_I16_PWL = 0, 1, 2, 3, 4
-PA_OK, PA_EINVAL, PA_ENOMEM, PA_EDEVICE, PA_ELAUNCH, PA_ERANGE = 0, -1, -2, -3, -4, -5
+PA_OK, PA_EINVAL, PA_ENOMEM, PA_EDEVICE, PA_ELAUNCH, PA_ERANGE, PA_ETOOBIG = 0, -1, -2, -3, -4, -5, -6
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libprefill_attn.so")
@@ -61,6 +62,8 @@ _SIGNATURES = {
                                             _P, ctypes.c_size_t, _P]),
     "prefill_attn_decode": (_I, [_P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _I, _P,
                                  ctypes.c_size_t, _P]),
+    "prefill_attn_decode_noalloc": (_I, [_P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _I, _P]),
+    "prefill_attn_decode_noalloc_scratch_bytes": (ctypes.c_size_t, []),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -276,6 +279,21 @@ def prefill_attn_decode(handle, in_dtype, batch, q, k_cache, v_cache, n_slots, k
                                               float(score_scale), n_split, _ptr(workspace), int(workspace_bytes),
                                               _stream(stream)),
            "prefill_attn_decode")
+
+
+def prefill_attn_decode_noalloc(handle, in_dtype, batch, q, k_cache, v_cache, n_slots, kv_map, map_stride,
+                                pos_offsets, out, score_scale=0.0, n_split=0, stream=None):
+    """Enqueue one decode pass with the partials in the library's fixed scratch (see the header)."""
+    _check(load_library().prefill_attn_decode_noalloc(handle, in_dtype, batch, _ptr(q), _ptr(k_cache),
+                                                      _ptr(v_cache), n_slots, _ptr(kv_map), map_stride,
+                                                      _ptr(pos_offsets), _ptr(out), float(score_scale), n_split,
+                                                      _stream(stream)),
+           "prefill_attn_decode_noalloc")
+
+
+def prefill_attn_decode_noalloc_scratch_bytes():
+    """Bytes of the fixed scratch that prefill_attn_decode_noalloc's partials use."""
+    return int(load_library().prefill_attn_decode_noalloc_scratch_bytes())
 
 
 # ------------------------------------------------------------- tensor helper

@@ -116,6 +116,12 @@ extern "C" int prefill_attn_init(prefill_attn** out, int n_heads, int n_kv_heads
         free_handle(h);
         return PA_ELAUNCH;
     }
+    // The no-allocation decode's scratch address on this device (looked up once).
+    float* scratch = nullptr;
+    if (pa::noalloc_scratch(&scratch) != hipSuccess) {
+        free_handle(h);
+        return PA_ELAUNCH;
+    }
     *out = h;
     return PA_OK;
 }
@@ -322,10 +328,15 @@ extern "C" size_t prefill_attn_decode_workspace_size(const prefill_attn* h, int 
     return n_split == 1 ? 0 : decode_ws_bytes(h, batch, n_split);
 }
 
-extern "C" int prefill_attn_decode(const prefill_attn* h, int in_dtype, int batch, const void* q,
-                                   const void* k_cache, const void* v_cache, int n_slots, const int32_t* kv_map,
-                                   int map_stride, const int32_t* pos_offsets, float* out, float score_scale,
-                                   int n_split, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Decode with the partials in `workspace` (workspace_bytes long).  strict: an
+// explicit n_split whose partials do not fit is an error (PA_ETOOBIG) instead
+// of being lowered.
+int decode_impl(const prefill_attn* h, int in_dtype, int batch, const void* q, const void* k_cache,
+                const void* v_cache, int n_slots, const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
+                float* out, float score_scale, int n_split, void* workspace, size_t workspace_bytes, bool strict,
+                void* stream) {
     if (!h || batch < 0 || n_split < 0) return PA_EINVAL;
     if (in_dtype != PA_IN_F32 && in_dtype != PA_IN_BF16) return PA_EINVAL;
     if (!std::isfinite(score_scale)) return PA_EINVAL;
@@ -344,6 +355,8 @@ extern "C" int prefill_attn_decode(const prefill_attn* h, int in_dtype, int batc
         const int target = kDecodeCUs * (G >= 8 ? 2 : 4);
         n_split = std::max(1, target / groups);
         n_split = std::min(n_split, std::max(1, map_stride / kDecodeMinKeysPerSplit));
+    } else if (strict && n_split > 1 && decode_ws_bytes(h, batch, n_split) > workspace_bytes) {
+        return PA_ETOOBIG;
     }
     if (n_split > 1 && (!workspace || workspace_bytes < decode_ws_bytes(h, batch, 2))) n_split = 1;
     while (n_split > 1 && decode_ws_bytes(h, batch, n_split) > workspace_bytes) --n_split;
@@ -371,6 +384,29 @@ extern "C" int prefill_attn_decode(const prefill_attn* h, int in_dtype, int batc
     hipError_t e = pa::launch_decode(h->head_dim, in_dtype == PA_IN_F32, a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
+
+}  // namespace
+
+extern "C" int prefill_attn_decode(const prefill_attn* h, int in_dtype, int batch, const void* q,
+                                   const void* k_cache, const void* v_cache, int n_slots, const int32_t* kv_map,
+                                   int map_stride, const int32_t* pos_offsets, float* out, float score_scale,
+                                   int n_split, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(h, in_dtype, batch, q, k_cache, v_cache, n_slots, kv_map, map_stride, pos_offsets, out,
+                       score_scale, n_split, workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int prefill_attn_decode_noalloc(const prefill_attn* h, int in_dtype, int batch, const void* q,
+                                           const void* k_cache, const void* v_cache, int n_slots,
+                                           const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
+                                           float* out, float score_scale, int n_split, void* stream) {
+    if (!h) return PA_EINVAL;
+    float* scratch = nullptr;
+    if (pa::noalloc_scratch(&scratch) != hipSuccess) return PA_ELAUNCH;
+    return decode_impl(h, in_dtype, batch, q, k_cache, v_cache, n_slots, kv_map, map_stride, pos_offsets, out,
+                       score_scale, n_split, scratch, pa::kNoAllocScratchBytes, true, stream);
+}
+
+extern "C" size_t prefill_attn_decode_noalloc_scratch_bytes(void) { return pa::kNoAllocScratchBytes; }
 
 extern "C" int prefill_attn_ring_map(int n_slots, int start, int count, int32_t* map) {
     if (n_slots < 1 || start < 0 || start >= n_slots || count < 0 || (count > 0 && !map)) return PA_EINVAL;
@@ -417,6 +453,7 @@ extern "C" const char* prefill_attn_strerror(int code) {
         case PA_EDEVICE: return "no usable gfx950 device";
         case PA_ELAUNCH: return "HIP runtime error";
         case PA_ERANGE: return "position outside the RoPE table or the index map, or a slot outside the cache";
+        case PA_ETOOBIG: return "the requested split does not fit the fixed scratch of the no-allocation call";
         default: return "unknown status code";
     }
 }

@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace pa {
@@ -426,6 +428,40 @@ hipError_t launch_split_merge(int head_dim, const DecodeArgs& a, hipStream_t s) 
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// Scratch of the no-allocation decode entry point: its split partials go here
+// instead of into a caller workspace.  Each device that the library runs on
+// holds one copy until the process ends; every call on a device shares it.
+// Host code never passes `scratch` itself (on the host that name is only a
+// stand-in for the symbol): it passes the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t noalloc_scratch(float** ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(int head_dim, bool f32, const DecodeArgs& a, hipStream_t s) {

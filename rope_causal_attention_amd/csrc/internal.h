@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace pa {
@@ -93,6 +94,12 @@ bool prefill_uses_eight_waves(const RunArgs& a);
 // Query heads served by one decode workgroup (a divisor of n_heads / n_kv_heads).
 int decode_group(int n_heads, int n_kv_heads);
 hipError_t launch_decode(int head_dim, bool f32, const DecodeArgs& a, hipStream_t stream);
+
+// Fixed scratch of the no-allocation decode call (split partials), in bytes.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+// Device address of that scratch on the current device; the symbol lookup
+// runs once per device (init, or the first call on another device).
+hipError_t noalloc_scratch(float** ptr);
 
 // Int16 test exports; RunArgs.q is the tensor to rotate (x) for the rope one,
 // q/k for the scores one; `dst` receives int16 x_rot or int32 scores.

@@ -110,6 +110,9 @@ def test_calls_on_null_handle():
     assert lib.prefill_attn_decode(None, pa.PA_IN_BF16, 1, 16, 16, 16, 8, 16, 4, None, 16, 0.0, 0, None, 0,
                                    None) == pa.PA_EINVAL
     assert lib.prefill_attn_decode_workspace_size(None, 4, 8) == 0
+    assert lib.prefill_attn_decode_noalloc(None, pa.PA_IN_BF16, 1, 16, 16, 16, 8, 16, 4, None, 16, 0.0, 0,
+                                           None) == pa.PA_EINVAL
+    assert lib.prefill_attn_decode_noalloc_scratch_bytes() == 8 << 20
 
 
 @pytest.mark.parametrize("n_slots,start,count", [(128, 120, 12), (8, 0, 8), (5, 4, 23), (1, 0, 3), (16, 3, 0)])
@@ -144,8 +147,8 @@ def test_map_builders_reject_bad_arguments():
 
 
 def test_strerror_covers_every_code():
-    texts = {c: pa.prefill_attn_strerror(c) for c in (0, -1, -2, -3, -4, -5)}
-    assert len(set(texts.values())) == 6
+    texts = {c: pa.prefill_attn_strerror(c) for c in (0, -1, -2, -3, -4, -5, -6)}
+    assert len(set(texts.values())) == 7
     assert pa.prefill_attn_strerror(-99) == "unknown status code"
 
 
