@@ -54,8 +54,15 @@ typedef struct prefill_attn prefill_attn; /* opaque handle */
 /* Input element types accepted by prefill_attn_run. */
 enum prefill_attn_dtype {
     PA_IN_F32 = 0,  /* Q, K, V float32; products on the fp32 matrix cores */
-    PA_IN_BF16 = 1, /* Q, K, V bfloat16; rotated Q'/K', P and V rounded to fp16 for the matrix cores, fp32 accumulate */
-    PA_IN_I16 = 2,  /* Q, K int16 fixed point, V bfloat16; integer RoPE, exact int32 scores, fp32 softmax */
+    PA_IN_BF16 = 1, /* Q, K, V bfloat16; rotated Q'/K', P and V rounded to fp16 for the matrix cores, fp32
+                       accumulate.  Range: V, K' = RoPE(K) and Q' = RoPE(Q) * score_scale * log2(e) must
+                       stay below 65504 in magnitude (every |x| < 2^15 is enough while score_scale <= 0.5);
+                       values below 2^-14 keep fewer bits (fp16 subnormals).  A larger K' or a non-finite O
+                       sets the status word (PA_EOVERFLOW from prefill_attn_status). */
+    PA_IN_I16 = 2,  /* Q, K int16 fixed point, V bfloat16; integer RoPE, exact int32 scores, fp32 softmax.
+                       Range: every rotated Q'/K' value must lie in [-8383, 8382] (the int8 digit split of
+                       the scores; |x| <= 5900 for every input is enough); outside it the scores are wrong
+                       and the status word is set (PA_EOVERFLOW).  V as for PA_IN_BF16. */
     PA_IN_BF16_Q16 = 3, /* Q, K, V bfloat16; each (token, head) row of Q and K quantised inside the kernel to
                           int16 codes, round-half-even(x * 2047 / max|x|) in fp32 (the 2kiu.com retelling, §3.3:
                           per-token dynamic activation scale), then the PA_IN_I16 path with
@@ -75,8 +82,12 @@ enum prefill_attn_status {
     PA_ELAUNCH = -4, /* the HIP runtime rejected a launch or a copy */
     PA_ERANGE = -5,  /* a run saw pos_offsets[b] < 0 or pos_offsets[b] + seq_len > max_seq (or, for the
                         cache calls, beyond map_stride, or a map entry outside the cache) */
-    PA_ETOOBIG = -6  /* prefill_attn_decode_noalloc: the requested split's partials exceed the
+    PA_ETOOBIG = -6, /* prefill_attn_decode_noalloc: the requested split's partials exceed the
                         library's fixed scratch */
+    PA_EOVERFLOW = -7 /* a run saw a value outside the range its kernel computes in: a non-finite
+                         O (bf16 path: an fp16 operand overflowed, or an input was not finite) or an
+                         fp16 K' = RoPE(K) beyond 65504, or (int16 path) a rotated Q'/K' value outside
+                         [-8383, 8382], where the int8 digit split wraps; O is not valid */
 };
 
 /*
@@ -86,9 +97,11 @@ enum prefill_attn_status {
  *   head_dim    64, 96 or 128
  *   max_seq     largest position + 1 any run may use (table rows), 1 .. 1048576
  *   rope_theta  RoPE base, > 1
- * Builds the RoPE cos/sin tables on the host in fp64 (rounded once to fp32 pairs
- * and to Q1.14 int16 pairs), copies them to the device and allocates the status
- * word.  All allocation happens here; prefill_attn_run allocates nothing.
+ * Builds the RoPE cos/sin tables on the host in fp64 (each value rounded once, to
+ * fp32 pairs for the fp32 path and decode, to fp16 pairs for the bf16 paths and
+ * to Q1.14 int16 pairs for the int16 paths), copies them to the device and
+ * allocates the status word.  All allocation happens here; prefill_attn_run
+ * allocates nothing.
  * On success *out receives the handle; on failure *out is set to NULL.
  */
 int prefill_attn_init(prefill_attn** out, int n_heads, int n_kv_heads, int head_dim,
@@ -262,7 +275,8 @@ int prefill_attn_paged_map(const int32_t* block_table, int n_blocks, int block_s
 /*
  * Synchronise `stream`, then report and clear the status word: PA_ERANGE if any
  * call since the last status call saw an out-of-range position, map row or
- * slot, else PA_OK.
+ * slot, else PA_EOVERFLOW if one saw a value outside its kernel's range (see
+ * PA_EOVERFLOW and the input types), else PA_OK.
  */
 int prefill_attn_status(prefill_attn* h, void* stream);
 
@@ -290,15 +304,21 @@ int prefill_attn_rope_table_q14(int max_seq, int head_dim, double rope_theta, in
 int prefill_attn_rope_table_f16(int max_seq, int head_dim, double rope_theta, uint16_t* out);
 
 /*
- * Test exports for the int16 variant: the same device code as PA_IN_I16 runs,
- * with an epilogue that writes intermediate results instead of O.
+ * Test exports for the int16 variant, run by the device code of PA_IN_I16:
  *   prefill_attn_debug_rope_i16: x [batch][seq_len][n_heads_x][head_dim] int16 ->
  *     x_rot (same shape) = (x C - y S + 2^13) >> 14, (x S + y C + 2^13) >> 14 at
  *     position pos_offsets[b] + i (the fixed-point rotation of the page titled
- *     "手写内核实现6倍prefill加速", §3.1, with Q1.14 tables).
- *   prefill_attn_debug_scores_i32: the full (unmasked) int32 score matrix
- *     scores[batch][n_heads][seq_len][seq_len], scores[b][h][i][j] = Q'[b,i,h] . K'[b,j,kvh(h)],
- *     computed by the int8 digit-split matrix-core path of PA_IN_I16.
+ *     "手写内核实现6倍prefill加速", §3.1, with Q1.14 tables), formed by the K staging
+ *     of the int16 kernels (table addressing, rotation, digit split into LDS) with
+ *     the staging width a prefill of this shape uses, and read back as 128 h + l
+ *     from the digit planes.  Values outside [-8383, 8382] set the status word
+ *     (PA_EOVERFLOW) and come back wrong.
+ *   prefill_attn_debug_scores_i32: the int32 scores of the causal part,
+ *     scores[b][h][i][j] = Q'[b,i,h] . K'[b,j,kvh(h)] for j <= i, of
+ *     scores[batch][n_heads][seq_len][seq_len] (entries j > i are not written),
+ *     stored by the very kernel prefill_attn_run launches for PA_IN_I16 at this
+ *     shape (eight-wave two-group or four-wave, the int8 digit-split matrix-core
+ *     path) from a debug instantiation that adds the store and writes no O.
  * Same pointer, alignment and stream rules as prefill_attn_run.
  */
 int prefill_attn_debug_rope_i16(const prefill_attn* h, int batch, int seq_len,
@@ -307,8 +327,8 @@ int prefill_attn_debug_rope_i16(const prefill_attn* h, int batch, int seq_len,
 int prefill_attn_debug_scores_i32(const prefill_attn* h, int batch, int seq_len,
                                   const int16_t* q, const int16_t* k, const int32_t* pos_offsets,
                                   int32_t* scores, void* stream);
-/* The same score matrix for bfloat16 Q/K through the in-kernel quantisation of
- * PA_IN_BF16_Q16: scores of the int16 codes. */
+/* The same causal scores for bfloat16 Q/K through the kernel of PA_IN_BF16_Q16
+ * (in-kernel quantisation): scores of the int16 codes. */
 int prefill_attn_debug_scores_q16(const prefill_attn* h, int batch, int seq_len,
                                   const void* q, const void* k, const int32_t* pos_offsets,
                                   int32_t* scores, void* stream);

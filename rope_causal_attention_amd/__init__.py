@@ -20,6 +20,7 @@ import torch
 __all__ = [
     "PA_IN_F32", "PA_IN_BF16", "PA_IN_I16", "PA_IN_BF16_Q16", "PA_IN_I16_PWL",
     "PA_OK", "PA_EINVAL", "PA_ENOMEM", "PA_EDEVICE", "PA_ELAUNCH", "PA_ERANGE", "PA_ETOOBIG",
+    "PA_EOVERFLOW",
     "PrefillAttnError", "load_library", "library_path",
     "prefill_attn_init", "prefill_attn_run", "prefill_attn_status", "prefill_attn_destroy",
     "prefill_attn_strerror", "prefill_attn_rope_table_f32", "prefill_attn_rope_table_q14",
@@ -33,7 +34,8 @@ __all__ = [
 ]
 
 PA_IN_F32, PA_IN_BF16, PA_IN_I16, PA_IN_BF16_Q16, PA_IN_I16_PWL = 0, 1, 2, 3, 4
-PA_OK, PA_EINVAL, PA_ENOMEM, PA_EDEVICE, PA_ELAUNCH, PA_ERANGE, PA_ETOOBIG = 0, -1, -2, -3, -4, -5, -6
+PA_OK, PA_EINVAL, PA_ENOMEM, PA_EDEVICE, PA_ELAUNCH, PA_ERANGE, PA_ETOOBIG, PA_EOVERFLOW = \
+    0, -1, -2, -3, -4, -5, -6, -7
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libprefill_attn.so")
@@ -158,9 +160,9 @@ def prefill_attn_run(handle, in_dtype, batch, seq_len, q, k, v, pos_offsets, out
 
 
 def prefill_attn_status(handle, stream=None):
-    """Synchronise the stream; return PA_OK or PA_ERANGE (and clear the flag)."""
+    """Synchronise the stream; return PA_OK, PA_ERANGE or PA_EOVERFLOW (and clear the flags)."""
     code = load_library().prefill_attn_status(handle, _stream(stream))
-    if code not in (PA_OK, PA_ERANGE):
+    if code not in (PA_OK, PA_ERANGE, PA_EOVERFLOW):
         raise PrefillAttnError(code, "prefill_attn_status")
     return code
 

@@ -435,7 +435,7 @@ extern "C" int prefill_attn_status(prefill_attn* h, void* stream) {
     if (hipMemcpy(&flag, h->d_status, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return PA_ELAUNCH;
     if (flag != 0 && hipMemset(h->d_status, 0, sizeof(int)) != hipSuccess) return PA_ELAUNCH;
     if (hipDeviceSynchronize() != hipSuccess) return PA_ELAUNCH;
-    return flag ? PA_ERANGE : PA_OK;
+    return (flag & 1) ? PA_ERANGE : (flag & 2) ? PA_EOVERFLOW : PA_OK;
 }
 
 extern "C" int prefill_attn_destroy(prefill_attn* h) {
@@ -454,6 +454,9 @@ extern "C" const char* prefill_attn_strerror(int code) {
         case PA_ELAUNCH: return "HIP runtime error";
         case PA_ERANGE: return "position outside the RoPE table or the index map, or a slot outside the cache";
         case PA_ETOOBIG: return "the requested split does not fit the fixed scratch of the no-allocation call";
+        case PA_EOVERFLOW:
+            return "an input value left the range the kernel computes in (fp16 operands of the bf16 path, "
+                   "int8 digits of the int16 path); the output is not valid";
         default: return "unknown status code";
     }
 }
@@ -482,6 +485,8 @@ int debug_scores(const prefill_attn* h, bool quant, int batch, int seq_len, cons
     if (!q || !k || !scores || !aligned16(q) || !aligned16(k) || !aligned16(scores)) return PA_EINVAL;
     a.q = q;
     a.k = k;
+    a.v = k;  // the score-export launch reads a V tensor of K's shape; its values do not reach the scores
+    a.score_scale = 1.0f;
     hipError_t e = quant ? pa::launch_debug_scores_q16(h->head_dim, a, scores, static_cast<hipStream_t>(stream))
                          : pa::launch_debug_scores_i32(h->head_dim, a, scores, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;

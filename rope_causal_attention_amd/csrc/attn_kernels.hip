@@ -268,9 +268,11 @@ struct Bf16QK {
         const char* tab;  // fp16 table row of position off[b] (2 D bytes per position)
         int S;
     };
+    // Q' and K' are fp16: the guard sees every converted value.
+    using Guard = F16Guard;
 
     // Rotate 4 adjacent pairs: x' = x c - y s, y' = x s + y c; times `scale`.
-    __device__ static __forceinline__ uint4 rotate8(const uint4& raw, const uint4& cs, float scale) {
+    __device__ static __forceinline__ uint4 rotate8(const uint4& raw, const uint4& cs, float scale, Guard& g) {
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
         const uint32_t t[4] = {cs.x, cs.y, cs.z, cs.w};
         uint32_t o[4];
@@ -280,6 +282,7 @@ struct Bf16QK {
             const float c = h_lo(t[j]), s = h_hi(t[j]);
             const float xr = fmaf(x, c, -y * s), yr = fmaf(x, s, y * c);
             o[j] = pack_h2(xr * scale, yr * scale);
+            g.add(o[j]);
         }
         return make_uint4(o[0], o[1], o[2], o[3]);
     }
@@ -290,7 +293,8 @@ struct Bf16QK {
                 reinterpret_cast<const char*>(a.rope_h2 + static_cast<size_t>(c.koff) * (D / 2)), c.NK};
     }
 
-    __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
+    __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q,
+                                                  Guard& g) {
         const int lh = (threadIdx.x & 63) >> 5;
         const bool ok = qi < c.S;
         const Rows rq = q_rows(a, c, a.q, D, 2);
@@ -303,7 +307,7 @@ struct Bf16QK {
                 raw = ld16(rq.base, qi * rq.stride + 2 * d0);
                 cs = ld16(tab, (qi * D + d0) * 2);
             }
-            q.f[ks] = __builtin_bit_cast(f16x8, rotate8(raw, cs, scale));
+            q.f[ks] = __builtin_bit_cast(f16x8, rotate8(raw, cs, scale, g));
         }
     }
 
@@ -326,23 +330,26 @@ struct Bf16QK {
     }
 
     // K' = RoPE(K) rounded once to fp16 (rot_pack_h2h).
-    __device__ static __forceinline__ uint4 rotate8_k(const uint4& raw, const uint4& cs) {
+    __device__ static __forceinline__ uint4 rotate8_k(const uint4& raw, const uint4& cs, Guard& g) {
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
         const uint32_t t[4] = {cs.x, cs.y, cs.z, cs.w};
         uint32_t o[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = rot_pack_h2h(bf_lo(w[j]), bf_hi(w[j]), t[j]);
+        for (int j = 0; j < 4; ++j) {
+            o[j] = rot_pack_h2h(bf_lo(w[j]), bf_hi(w[j]), t[j]);
+            g.add(o[j]);
+        }
         return make_uint4(o[0], o[1], o[2], o[3]);
     }
 
-    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
+    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds, Guard& g) {
         _Float16* kl = reinterpret_cast<_Float16*>(lds);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             if (!has(i)) continue;
             const int idx = static_cast<int>(threadIdx.x % NT) + NT * i;
             const int row = idx / (D / 8), ch = idx % (D / 8);
-            *reinterpret_cast<uint4*>(kl + row * kStride + 8 * ch) = rotate8_k(r.raw[i], r.cs[i]);
+            *reinterpret_cast<uint4*>(kl + row * kStride + 8 * ch) = rotate8_k(r.raw[i], r.cs[i], g);
         }
     }
 
@@ -388,12 +395,15 @@ struct I16QK {
         const char* tab;
         int S;
     };
+    // The digit split is exact only for rotated values in [kDigitMin, kDigitMax].
+    using Guard = DigitGuard;
 
     // Fixed-point rotation with round-half-up: (x C - y S + 2^13) >> 14, (x S + y C + 2^13) >> 14.
     __device__ static __forceinline__ int rot_x(int x, int y, int C, int S) { return (x * C - y * S + 8192) >> 14; }
     __device__ static __forceinline__ int rot_y(int x, int y, int C, int S) { return (x * S + y * C + 8192) >> 14; }
 
-    // a = 128 h + l, l in [-64, 63]; returns the three digit bytes h, l, h + l.
+    // a = 128 h + l, l in [-64, 63]; returns the three digit bytes h, l, h + l
+    // (all three are int8 for a in [-8383, 8382]: at 8383, h + l = 65 + 63 wraps).
     __device__ static __forceinline__ void split(int a, uint32_t& h, uint32_t& l, uint32_t& m) {
         const int lo = ((a + 64) & 127) - 64;
         const int hi = (a - lo) >> 7;
@@ -403,9 +413,10 @@ struct I16QK {
     }
 
     // Rotate 4 pairs (one uint4 of int16) with 4 (C, S) pairs and split into digits:
-    // 8 bytes per plane returned as two dwords each.
+    // 8 bytes per plane returned as two dwords each; the guard sees the rotated values.
+    template <class G>
     __device__ static __forceinline__ void rotate_split8(const uint4& raw, const uint4& cs, uint2& h, uint2& l,
-                                                         uint2& m) {
+                                                         uint2& m, G& g) {
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
         const uint32_t t[4] = {cs.x, cs.y, cs.z, cs.w};
         uint32_t hb[2] = {0, 0}, lb[2] = {0, 0}, mb[2] = {0, 0};
@@ -414,6 +425,7 @@ struct I16QK {
             const int x = i16_lo(w[j]), y = i16_hi(w[j]);
             const int C = i16_lo(t[j]), S = i16_hi(t[j]);
             const int xr = rot_x(x, y, C, S), yr = rot_y(x, y, C, S);
+            g.add(xr, yr);
             uint32_t a0, a1, a2, b0, b1, b2;
             split(xr, a0, a1, a2);
             split(yr, b0, b1, b2);
@@ -433,7 +445,8 @@ struct I16QK {
                 reinterpret_cast<const char*>(a.rope_q14 + static_cast<size_t>(c.koff) * D), c.NK};
     }
 
-    __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
+    __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q,
+                                                  Guard& g) {
         const int lh = (threadIdx.x & 63) >> 5;
         const bool ok = qi < c.S;
         const Rows rq = q_rows(a, c, a.q, D, 2);
@@ -450,7 +463,7 @@ struct I16QK {
                     raw = ld16(rq.base, qi * rq.stride + 2 * (d0 + 8 * half));
                     cs = ld16(tab, (qi * D + d0 + 8 * half) * 2);
                 }
-                rotate_split8(raw, cs, h[half], l[half], m[half]);
+                rotate_split8(raw, cs, h[half], l[half], m[half], g);
             }
             q.h[ks] = i32x4{(int)h[0].x, (int)h[0].y, (int)h[1].x, (int)h[1].y};
             q.l[ks] = i32x4{(int)l[0].x, (int)l[0].y, (int)l[1].x, (int)l[1].y};
@@ -475,14 +488,14 @@ struct I16QK {
         }
     }
 
-    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
+    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds, Guard& g) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             if (!has(i)) continue;
             const int idx = static_cast<int>(threadIdx.x % NT) + NT * i;
             const int row = idx / (D / 8), ch = idx % (D / 8);
             uint2 h, l, m;
-            rotate_split8(r.raw[i], r.cs[i], h, l, m);
+            rotate_split8(r.raw[i], r.cs[i], h, l, m, g);
             char* p = lds + row * kRow + 8 * ch;
             *reinterpret_cast<uint2*>(p) = h;
             *reinterpret_cast<uint2*>(p + kPlane) = l;
@@ -511,12 +524,15 @@ struct I16QK {
         }
     }
 
-    // Logits (log2 units): float(score) * scale.
+    // Logits (log2 units) of key block kb from its int32 scores: float(score) * scale.
+    __device__ static __forceinline__ void logits(const char*, int, const Q& q, const int* si, float* s, int) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = static_cast<float>(si[v]) * q.scale;
+    }
     __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh) {
         int si[16];
         qk_i32(lds, kb, q, si, lq, lh);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] = static_cast<float>(si[v]) * q.scale;
+        logits(lds, kb, q, si, s, lh);
     }
 };
 
@@ -568,6 +584,8 @@ struct I16QuantQK : I16QK<D, NT> {
     static_assert(BN * 16 % NT == 0, "whole passes");
     using Q = typename Base::Q;
     using KPtr = typename Base::KPtr;
+    // Codes in [-2048, 2047] rotate to at most 2897 in magnitude: always exact.
+    using Guard = NoGuard;
     struct KRegs {
         uint32_t raw[kPasses][E / 2];  // bf16 pairs
         uint32_t cs[kPasses][E / 2];   // Q1.14 (C, S) pairs
@@ -580,7 +598,8 @@ struct I16QuantQK : I16QK<D, NT> {
 
     // Q: the lane holds dims 32 ks + 16 lh .. +15 of query qi; the row max
     // comes from both lane halves.
-    __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q) {
+    __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q,
+                                                  Guard& g) {
         const int lh = (threadIdx.x & 63) >> 5;
         const bool ok = qi < c.S;
         const Rows rq = q_rows(a, c, a.q, D, 2);
@@ -612,7 +631,8 @@ struct I16QuantQK : I16QK<D, NT> {
                 for (int j = 0; j < 4; ++j)
                     cw[j] = (static_cast<uint32_t>(quant_code(bf_lo(w[j]), qs)) & 0xffffu) |
                             (static_cast<uint32_t>(quant_code(bf_hi(w[j]), qs)) << 16);
-                Base::rotate_split8(make_uint4(cw[0], cw[1], cw[2], cw[3]), cs[ks][half], h[half], l[half], mm[half]);
+                Base::rotate_split8(make_uint4(cw[0], cw[1], cw[2], cw[3]), cs[ks][half], h[half], l[half], mm[half],
+                                    g);
             }
             q.h[ks] = i32x4{(int)h[0].x, (int)h[0].y, (int)h[1].x, (int)h[1].y};
             q.l[ks] = i32x4{(int)l[0].x, (int)l[0].y, (int)l[1].x, (int)l[1].y};
@@ -641,7 +661,7 @@ struct I16QuantQK : I16QK<D, NT> {
         }
     }
 
-    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
+    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds, Guard&) {
         const int tid = threadIdx.x % NT;
         const int sub = tid & 15;
 #pragma unroll
@@ -684,10 +704,14 @@ struct I16QuantQK : I16QK<D, NT> {
         }
     }
 
-    // Logits (log2 units): float(score) * scale_q * m_k / 2047 of each key.
+    // Logits (log2 units) from the int32 scores: float(score) * scale_q * m_k / 2047 of each key.
     __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh) {
         int si[16];
         Base::qk_i32(lds, kb, q, si, lq, lh);
+        logits(lds, kb, q, si, s, lh);
+    }
+    __device__ static __forceinline__ void logits(const char* lds, int kb, const Q& q, const int* si, float* s,
+                                                  int lh) {
         const float* inv = reinterpret_cast<const float*>(lds + kInv) + 32 * kb + 4 * lh;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -736,7 +760,7 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
             r.cs[i] = *reinterpret_cast<const uint2*>(tb + (row * D + e0 + 4 * i) * 2);
         }
     }
-    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds) {
+    __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds, typename Base::Guard& g) {
         const int tid = threadIdx.x % NT;
         const int row = tid >> 3;
         const int e0 = (tid & 7) * (D / 8);
@@ -747,7 +771,10 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
             const uint32_t t[2] = {r.cs[i].x, r.cs[i].y};
             uint32_t o[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) o[j] = rot_pack_h2h(bf_lo(w[j]), bf_hi(w[j]), t[j]);
+            for (int j = 0; j < 2; ++j) {
+                o[j] = rot_pack_h2h(bf_lo(w[j]), bf_hi(w[j]), t[j]);
+                g.add(o[j]);
+            }
             *reinterpret_cast<uint2*>(kl + 4 * i) = make_uint2(o[0], o[1]);
         }
     }
@@ -817,8 +844,13 @@ struct VStage8 : VStage<D, NT> {
 // staged three tiles ahead and V two): a buffer is rewritten only after the
 // barrier that follows its last read, and a tile is whole one barrier before
 // it is read.
+//
+// DBG (int16 score paths, plain launches): the kernel also stores every
+// int32 score it forms for a key at or before its query to a.dbg_scores
+// [B][Hq][S][S], and stores no O; V may then be any readable tensor of K's
+// shape (its values do not reach the scores).
 template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, bool MAPPED, bool SPLIT,
-          bool PWL = false, bool PP = false, bool PAIR = false, int GP = 1>
+          bool PWL = false, bool PP = false, bool PAIR = false, int GP = 1, bool DBG = false>
 struct FusedAttn {
     static constexpr int NT = 64 * NW;
     static constexpr int BMW = 32 * NW;
@@ -847,6 +879,7 @@ struct FusedAttn {
     typename P::KRegs kr;
     typename V::Regs vr;
     typename P::Q q;
+    typename P::Guard guard;  // range of this thread's converted Q' / K' values
     f32x16 o[D / 32];
     float m_run, l_a, l_b;
 
@@ -868,10 +901,33 @@ struct FusedAttn {
     template <bool FULL>
     __device__ __forceinline__ void qk_tile(int t, float* s) const {
         const int na = FULL ? 2 : nact(t);
-        if (na >= 1) P::qk(kbuf(t), 0, q, s, lq, lh);
-        if (P::kSerialBlocks) __builtin_amdgcn_sched_barrier(0);
-        if (na == 2) P::qk(kbuf(t), 1, q, s + 16, lq, lh);
+        if constexpr (DBG) {
+            if (na >= 1) qk_store(t, 0, s);
+            if (na == 2) qk_store(t, 1, s + 16);
+        } else {
+            if (na >= 1) P::qk(kbuf(t), 0, q, s, lq, lh);
+            if (P::kSerialBlocks) __builtin_amdgcn_sched_barrier(0);
+            if (na == 2) P::qk(kbuf(t), 1, q, s + 16, lq, lh);
+        }
     }
+    // DBG: the int32 scores of key block kb, stored for keys at or before the
+    // lane's query, then turned into logits as P::qk does.
+    __device__ __forceinline__ void qk_store(int t, int kb, float* s) const {
+        int si[16];
+        P::qk_i32(kbuf(t), kb, q, si, lq, lh);
+        const int qi = qw0 + lq;
+        if (qi < c.S) {
+            int32_t* row = a_dbg + ((static_cast<size_t>(c.b) * n_heads_dbg + c.hq) * c.S + qi) * c.S;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = t * BN + 32 * kb + acc_row(v, lh);
+                if (key <= qi) row[key] = si[v];
+            }
+        }
+        P::logits(kbuf(t), kb, q, si, s, lh);
+    }
+    int32_t* a_dbg = nullptr;  // DBG: the score matrix, and the query head count of its layout
+    int n_heads_dbg = 0;
 
     template <bool FULL>
     __device__ __forceinline__ void softmax(int t, int na, float* s, uint32_t* pk) {
@@ -1026,7 +1082,7 @@ struct FusedAttn {
         }
         if (STEADY || t + 1 < n_tiles) qk_tile<STEADY>(t + 1, sn);
         if (na > 0) pv_tile(t, na, pk);
-        if (ld_k) P::commit_k(kr, kbuf(t + KA));
+        if (ld_k) P::commit_k(kr, kbuf(t + KA), guard);
         if (ld_v) V::commit(vr, vbuf(t + VA));
         if (!PAIR || bar) __syncthreads();
     }
@@ -1070,7 +1126,7 @@ struct FusedAttn {
     }
     template <bool STEADY>
     __device__ __forceinline__ int vector_phase(int t, float* s, uint32_t* pk) {
-        if (STEADY || t + 2 < n_tiles) P::commit_k(kr, kbuf(t + 2));
+        if (STEADY || t + 2 < n_tiles) P::commit_k(kr, kbuf(t + 2), guard);
         if (STEADY || t + 1 < n_tiles) V::commit(vr, vbuf(t + 1));
         if (STEADY || t + 3 < n_tiles) P::template load_k<!STEADY, MAPPED>(kp, t + 3, kr);
         if (STEADY || t + 2 < n_tiles) V::template load<!STEADY, MAPPED>(vp, c.NK, t + 2, vr);
@@ -1122,12 +1178,12 @@ struct FusedAttn {
             V::template load<true, MAPPED>(vp, c.NK, t_lo + 1, vr);
         }
         if (t_lo + 2 < n_tiles) P::template load_k<true, MAPPED>(kp, t_lo + 2, kr);
-        P::load_q(a, c, qw0 + lq, logit_scale, q);
+        P::load_q(a, c, qw0 + lq, logit_scale, q, guard);
         if (any) {
-            P::commit_k(kr0, kbuf(t_lo));
+            P::commit_k(kr0, kbuf(t_lo), guard);
             V::commit(vr0, vbuf(t_lo));
         }
-        if (t_lo + 1 < n_tiles) P::commit_k(kr1, kbuf(t_lo + 1));
+        if (t_lo + 1 < n_tiles) P::commit_k(kr1, kbuf(t_lo + 1), guard);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
         m_run = kNegInf;
@@ -1161,33 +1217,50 @@ struct FusedAttn {
         finish(a);
     }
 
+    // Bit 1 of the status word: a converted Q' / K' left its range (this
+    // thread's guard) or a row of O (or of a partial) is not finite.
+    __device__ __forceinline__ void report_range(const RunArgs& a, bool bad) const {
+        if (bad) atomicOr(a.status, 2);
+    }
+
     // Normalised O (or the split-K partial) of the wave's rows.
     __device__ __forceinline__ void finish(const RunArgs& a) {
-        if (qw0 >= c.S) return;
+        const bool gbad = guard.bad();
+        if (DBG || qw0 >= c.S) {
+            report_range(a, gbad);
+            return;
+        }
         if (SPLIT) {
             // A row that saw no key of this split (its first tile starts past
             // the row) keeps m_run = -inf: an empty partial.
             const float l = halves_sum(l_a + l_b);  // cross-lane: every lane takes part
             if (m_run == kNegInf) {
+                report_range(a, gbad);
                 empty_partials(a);
                 return;
             }
             const int qi = qw0 + lq;
+            bool bad = gbad || !__builtin_isfinite(l);
             if (qi < c.S) {
                 const size_t row = q_index(a, c, qi, D) / D;
                 float* dst = split_o(a, row, c.split, D);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        *reinterpret_cast<float4*>(dst + 32 * db + 8 * g + 4 * lh) =
-                            make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 val = make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2],
+                                                       o[db][4 * g + 3]);
+                        bad |= !__builtin_isfinite(val.x + val.y + val.z + val.w);
+                        *reinterpret_cast<float4*>(dst + 32 * db + 8 * g + 4 * lh) = val;
+                    }
                 if (lh == 0) *split_ml(a, row, c.split, D) = make_float2(m_run, l);
             }
+            report_range(a, bad);
             return;
         }
         const float inv = PWL ? newton_reciprocal(halves_sum(l_a + l_b)) : 1.0f / halves_sum(l_a + l_b);
         const int qi = qw0 + lq;
+        bool bad = gbad;
         if (qi < c.S) {
             float* orow = a.out + q_index(a, c, qi, D);
 #pragma unroll
@@ -1196,9 +1269,11 @@ struct FusedAttn {
                 for (int g = 0; g < 4; ++g) {
                     const float4 val = make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
                                                    o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                    bad |= !__builtin_isfinite(val.x + val.y + val.z + val.w);
                     *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * lh) = val;
                 }
         }
+        report_range(a, bad);
     }
 
     __device__ __forceinline__ void run(const RunArgs& a, float logit_scale) {
@@ -1225,11 +1300,11 @@ struct FusedAttn {
         float pwl_max = kNegInf;
         if (PWL) {
             // First pass: the maximum visible logit of every query row.
-            P::load_q(a, c, qw0 + lq, logit_scale, q);
+            P::load_q(a, c, qw0 + lq, logit_scale, q, guard);
             for (int t = 0; t < n_tiles; ++t) {
                 P::template load_k<true, MAPPED>(kp, t, kr);
                 __syncthreads();  // the previous tile's reads are done
-                P::commit_k(kr, kbuf(0));
+                P::commit_k(kr, kbuf(0), guard);
                 __syncthreads();
                 const int na = nact(t);
                 float s1[32];
@@ -1256,14 +1331,14 @@ struct FusedAttn {
         if (k1) P::template load_k<true, MAPPED>(kp, t_lo + 1, kr1);
         if (v1) V::template load<true, MAPPED>(vp, c.NK, t_lo + 1, vr1);
         if (k2) P::template load_k<true, MAPPED>(kp, t_lo + 2, kr2);
-        P::load_q(a, c, qw0 + lq, logit_scale, q);
+        P::load_q(a, c, qw0 + lq, logit_scale, q, guard);
         if (any) {
-            P::commit_k(kr, kbuf(t_lo));
+            P::commit_k(kr, kbuf(t_lo), guard);
             V::commit(vr, vbuf(t_lo));
         }
-        if (k1) P::commit_k(kr1, kbuf(t_lo + 1));
+        if (k1) P::commit_k(kr1, kbuf(t_lo + 1), guard);
         if (v1) V::commit(vr1, vbuf(t_lo + 1));
-        if (k2) P::commit_k(kr2, kbuf(t_lo + 2));
+        if (k2) P::commit_k(kr2, kbuf(t_lo + 2), guard);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
         m_run = PWL ? pwl_max : kNegInf;
@@ -1295,14 +1370,18 @@ struct FusedAttn {
 };
 
 template <int D, template <int, int> class QKT, template <int, int> class VST, int NW, int MINB, bool MAPPED,
-          bool SPLIT = false, bool PWL = false, bool PP = false, bool PAIR = false, int GP = 1>
+          bool SPLIT = false, bool PWL = false, bool PP = false, bool PAIR = false, int GP = 1, bool DBG = false>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, float logit_scale) {
-    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT, PWL, PP, PAIR, GP>;
+    using K = FusedAttn<D, QKT, VST, NW, MAPPED, SPLIT, PWL, PP, PAIR, GP, DBG>;
     __shared__ __attribute__((aligned(16))) char lds[K::kLds];
     __shared__ float knots[PWL ? 9 : 1];
     K k;
     k.lds = lds;
     k.knots = knots;
+    if (DBG) {
+        k.a_dbg = a.dbg_scores;
+        k.n_heads_dbg = a.n_heads;
+    }
     if (PWL && threadIdx.x < 9) {
         // e^-n, n = 0..8
         constexpr float kE[9] = {1.0f, 0.36787944117144233f, 0.1353352832366127f, 0.049787068367863944f,
@@ -1339,6 +1418,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, floa
     const BlockPos bp = block(0);
     const bool ok = make_ctx_at<K::BMP, MAPPED>(a, bp, split, k.c);
     if (!ok) {
+        if (DBG) {
+            if (threadIdx.x == 0) atomicOr(a.status, 1);  // no O to zero
+            return;
+        }
         zero_block();
     } else {
         k.c.hq += hw;
@@ -1522,69 +1605,51 @@ __global__ __launch_bounds__(kThreads) void kv_cache_update_kernel(RunArgs a, ui
 
 // ------------------------------------------------ int16 test kernels
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void debug_rope_i16_kernel(RunArgs a, int n_heads_x, int16_t* dst) {
-    const size_t pair = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
-    const size_t total = static_cast<size_t>(a.batch) * a.seq_len * n_heads_x * (D / 2);
-    if (pair >= total) return;
-    const int k = static_cast<int>(pair % (D / 2));
-    size_t rest = pair / (D / 2);
-    rest /= n_heads_x;
-    const int i = static_cast<int>(rest % a.seq_len);
-    const int b = static_cast<int>(rest / a.seq_len);
-    const int off = a.pos_offsets ? a.pos_offsets[b] : 0;
-    const int16_t* src = static_cast<const int16_t*>(a.q);
-    if (off < 0 || static_cast<long long>(off) + a.seq_len > a.max_seq) {
-        dst[2 * pair] = 0;
-        dst[2 * pair + 1] = 0;
-        atomicOr(a.status, 1);
-        return;
-    }
-    const int x = src[2 * pair], y = src[2 * pair + 1];
-    const int16_t* t = a.rope_q14 + static_cast<size_t>(off + i) * D + 2 * k;
-    dst[2 * pair] = static_cast<int16_t>(I16QK<D, kThreads>::rot_x(x, y, t[0], t[1]));
-    dst[2 * pair + 1] = static_cast<int16_t>(I16QK<D, kThreads>::rot_y(x, y, t[0], t[1]));
-}
-
-// Full (unmasked) int32 score matrix through the same staging and MFMA code
-// (int16 inputs, or bf16 inputs quantised in-kernel).
-template <int D, template <int, int> class QKT>
-__global__ __launch_bounds__(kThreads) void debug_scores_i32_kernel(RunArgs a, int32_t* dst) {
-    using P = QKT<D, kThreads>;
+// RoPE of int16 rows through the int16 path's own K staging: a workgroup of
+// NT threads (the NT of the prefill launch of this shape) loads one 64-row tile
+// of one (batch, head) with its Q1.14 table rows (load_k), rotates it and
+// splits it into the three digit planes in LDS (commit_k, rotate_split8), and
+// writes back x' = 128 h + l read from the planes.  a.k is the input,
+// a.n_kv_heads its head count.
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void debug_rope_i16_kernel(RunArgs a, int16_t* dst) {
+    using P = I16QK<D, NT>;
     __shared__ __attribute__((aligned(16))) char lds[P::kBytes];
+    const int n_tiles = (a.seq_len + BN - 1) / BN;
+    const int tile = static_cast<int>(blockIdx.x) % n_tiles;
+    const int bh = static_cast<int>(blockIdx.x) / n_tiles;
     Ctx c;
-    if (!make_ctx<BM, false>(a, c)) {
+    c.b = bh / a.n_kv_heads;
+    c.hkv = bh % a.n_kv_heads;
+    c.hq = c.hkv;
+    c.S = a.seq_len;
+    c.q0 = 0;
+    c.off = a.pos_offsets ? a.pos_offsets[c.b] : 0;
+    c.koff = c.off;
+    c.kshift = 0;
+    c.NK = c.S;
+    c.split = 0;
+    const int rows = min(BN, c.S - tile * BN);
+    int16_t* out = dst + kv_index(a, c, tile * BN, D);
+    const uint32_t stride = static_cast<uint32_t>(a.n_kv_heads) * D;
+    if (c.off < 0 || static_cast<long long>(c.off) + c.S > a.max_seq) {
+        for (int idx = threadIdx.x; idx < rows * D; idx += NT) out[(idx / D) * stride + idx % D] = 0;
         if (threadIdx.x == 0) atomicOr(a.status, 1);
         return;
     }
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int lq = lane & 31, lh = lane >> 5;
-    const int qw0 = c.q0 + 32 * w;
-    typename P::Q q;
-    P::load_q(a, c, qw0 + lq, 1.0f, q);
-    const int n_tiles = (c.S + BN - 1) / BN;
     const typename P::KPtr kp = P::template kptr<false>(a, c);
-    for (int t = 0; t < n_tiles; ++t) {
-        typename P::KRegs kr;
-        P::template load_k<true, false>(kp, t, kr);
-        __syncthreads();
-        P::commit_k(kr, lds);
-        __syncthreads();
-        // Every lane takes part in the MFMAs (a lane's A operand feeds the other
-        // lanes' results); only the stores are limited to real queries and keys.
-        const int qi = qw0 + lq;
-        int32_t* row = dst + ((static_cast<size_t>(c.b) * a.n_heads + c.hq) * c.S + min(qi, c.S - 1)) * c.S;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            int s[16];
-            P::qk_i32(lds, kb, q, s, lq, lh);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = t * BN + 32 * kb + acc_row(v, lh);
-                if (qi < c.S && key < c.S) row[key] = s[v];
-            }
-        }
+    typename P::KRegs kr;
+    typename P::Guard g;
+    P::template load_k<true, false>(kp, tile, kr);
+    P::commit_k(kr, lds, g);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < rows * D; idx += NT) {
+        const int r = idx / D, d = idx % D;
+        const int h = static_cast<int8_t>(lds[r * P::kRow + d]);
+        const int l = static_cast<int8_t>(lds[P::kPlane + r * P::kRow + d]);
+        out[r * stride + d] = static_cast<int16_t>(128 * h + l);
     }
+    if (g.bad()) atomicOr(a.status, 2);
 }
 
 // ------------------------------------------------ launch helpers
@@ -1684,7 +1749,8 @@ hipError_t launch_bf16_d(const RunArgs& a, hipStream_t s) {
         launch_bf16_dm<D, false, false>(a, s);
     return hipGetLastError();
 }
-template <int D, template <int, int> class QKT>
+// DBG: the same launch with the score-storing instantiation (plain launches only).
+template <int D, template <int, int> class QKT, bool DBG = false>
 hipError_t launch_int_d(const RunArgs& a, hipStream_t s) {
     // Plain head_dim 128 launches that fill the chip run the eight-wave
     // two-group kernel (half the K staging and quantisation per query row); at
@@ -1697,10 +1763,16 @@ hipError_t launch_int_d(const RunArgs& a, hipStream_t s) {
                 b.paired = 1;
                 g.x = static_cast<unsigned>(((a.seq_len + 255) / 256 + 1) / 2) * a.batch * a.n_heads;
             }
-            hipLaunchKernelGGL((attn_fwd_kernel<D, QKT, VStage8, 8, 1, false, false, false, true>), g, dim3(512), 0, s,
-                               b, a.score_scale * kLog2e);
+            hipLaunchKernelGGL((attn_fwd_kernel<D, QKT, VStage8, 8, 1, false, false, false, true, false, 1, DBG>), g,
+                               dim3(512), 0, s, b, a.score_scale * kLog2e);
             return hipGetLastError();
         }
+    }
+    if constexpr (DBG) {
+        if (a.kv_map) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((attn_fwd_kernel<D, QKT, VStage, 4, 1, false, false, false, false, false, 1, true>),
+                           grid_for(a, 128), dim3(256), 0, s, a, a.score_scale * kLog2e);
+        return hipGetLastError();
     }
     if (a.kv_map && a.n_split > 1) {
         dim3 g = grid_for(a, 128);
@@ -1774,24 +1846,34 @@ hipError_t launch_kv_cache_update(int head_dim, int el, const RunArgs& a, void* 
 }
 
 namespace {
+// The staging width (threads per workgroup) that prefill_attn_run uses for
+// int16 inputs of this shape: 512 for eight-wave head_dim 128 launches.
 template <int D>
 hipError_t launch_rope_d(const RunArgs& a, int n_heads_x, int16_t* dst, hipStream_t s) {
-    const size_t pairs = static_cast<size_t>(a.batch) * a.seq_len * n_heads_x * (D / 2);
-    const size_t blocks = (pairs + kThreads - 1) / kThreads;
-    if (blocks > 0x7fffffffu) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((debug_rope_i16_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a,
-                       n_heads_x, dst);
+    RunArgs b = a;
+    b.k = a.q;
+    b.n_heads = n_heads_x;
+    b.n_kv_heads = n_heads_x;
+    const long long blocks = static_cast<long long>((a.seq_len + BN - 1) / BN) * a.batch * n_heads_x;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 g(static_cast<unsigned>(blocks));
+    if (D == 128 && prefill_uses_eight_waves(b))
+        hipLaunchKernelGGL((debug_rope_i16_kernel<D, 512>), g, dim3(512), 0, s, b, dst);
+    else
+        hipLaunchKernelGGL((debug_rope_i16_kernel<D, 256>), g, dim3(256), 0, s, b, dst);
     return hipGetLastError();
 }
 template <int D>
 hipError_t launch_scores_d(const RunArgs& a, int32_t* dst, hipStream_t s) {
-    hipLaunchKernelGGL((debug_scores_i32_kernel<D, I16QK>), grid_for(a, BM), dim3(kThreads), 0, s, a, dst);
-    return hipGetLastError();
+    RunArgs b = a;
+    b.dbg_scores = dst;
+    return launch_int_d<D, I16QK, true>(b, s);
 }
 template <int D>
 hipError_t launch_scores_q_d(const RunArgs& a, int32_t* dst, hipStream_t s) {
-    hipLaunchKernelGGL((debug_scores_i32_kernel<D, I16QuantQK>), grid_for(a, BM), dim3(kThreads), 0, s, a, dst);
-    return hipGetLastError();
+    RunArgs b = a;
+    b.dbg_scores = dst;
+    return launch_int_d<D, I16QuantQK, true>(b, s);
 }
 }  // namespace
 

@@ -51,6 +51,35 @@ __device__ __forceinline__ uint32_t rot_pack_h2h(float x, float y, uint32_t cs) 
     asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(x), "v"(cs), "v"(yc));
     return r;
 }
+// Range guards of the narrowing conversions; bad() is this thread's verdict.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// fp16 results (packed pairs): the running maximum of their magnitude bits;
+// a half at 0x7c00 or above is inf or NaN (the value left the fp16 range).
+struct F16Guard {
+    uint32_t m = 0;
+    __device__ __forceinline__ void add(uint32_t h2) {
+        m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, m),
+                                                                   __builtin_bit_cast(u16x2, h2 & 0x7fff7fffu)));
+    }
+    __device__ __forceinline__ bool bad() const { return (m & 0xffffu) >= 0x7c00u || (m >> 16) >= 0x7c00u; }
+};
+// Rotated int16 values split into int8 digits h, l and h + l (a = 128 h + l,
+// l in [-64, 63]): all three fit int8 for every a in [-8383, 8382].
+constexpr int kDigitMax = 8382, kDigitMin = -8383;
+struct DigitGuard {
+    int mx = 0, mn = 0;
+    __device__ __forceinline__ void add(int a, int b) {
+        mx = max(mx, max(a, b));
+        mn = min(mn, min(a, b));
+    }
+    __device__ __forceinline__ bool bad() const { return mx > kDigitMax || mn < kDigitMin; }
+};
+// Inputs that cannot leave the range (codes quantised to [-2048, 2047]).
+struct NoGuard {
+    __device__ __forceinline__ void add(int, int) {}
+    __device__ __forceinline__ bool bad() const { return false; }
+};
+
 __device__ __forceinline__ float h_lo(uint32_t w) { return static_cast<float>(__builtin_bit_cast(f16x2, w)[0]); }
 __device__ __forceinline__ float h_hi(uint32_t w) { return static_cast<float>(__builtin_bit_cast(f16x2, w)[1]); }
 

@@ -17,7 +17,7 @@ struct RunArgs {
     const float* rope_f32;       // [max_seq][head_dim/2] (cos, sin) fp32 pairs
     const int16_t* rope_q14;     // [max_seq][head_dim/2] (C, S) Q1.14 pairs
     const uint32_t* rope_h2;     // [max_seq][head_dim/2] (cos, sin) fp16 pairs, cos in the low half
-    int* status;                 // set non-zero when a position leaves the table
+    int* status;                 // bit 0: a position left the table or map; bit 1: a value left its range
     int batch;
     int seq_len;
     int n_heads;
@@ -40,6 +40,9 @@ struct RunArgs {
     // runs query block n_qblocks - 1 - j and then block j, so every pair
     // covers the same number of key tiles.
     int paired;
+    // Score-export launches of the int16 paths only: [batch][n_heads][S][S] int32
+    // scores of every key at or before its query (no O is written).
+    int32_t* dbg_scores;
 };
 
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t stream);

@@ -147,8 +147,8 @@ def test_map_builders_reject_bad_arguments():
 
 
 def test_strerror_covers_every_code():
-    texts = {c: pa.prefill_attn_strerror(c) for c in (0, -1, -2, -3, -4, -5, -6)}
-    assert len(set(texts.values())) == 7
+    texts = {c: pa.prefill_attn_strerror(c) for c in (0, -1, -2, -3, -4, -5, -6, -7)}
+    assert len(set(texts.values())) == 8
     assert pa.prefill_attn_strerror(-99) == "unknown status code"
 
 

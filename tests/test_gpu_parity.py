@@ -137,6 +137,28 @@ def _i16_handle(w, max_seq=None):
     return pa.PrefillAttention(w.n_heads, w.n_kv_heads, w.head_dim, max_seq or w.seq_len, w.rope_theta)
 
 
+UNWRITTEN = -2 ** 31  # score-export buffers start filled with this
+
+
+def _score_buffer(B, H, S):
+    return torch.full((B, H, S, S), UNWRITTEN, dtype=torch.int32, device="cuda")
+
+
+def _assert_causal_scores(got, want, what):
+    """got: the export's [S][S] block; want: the oracle's full [S][S] scores.
+    Keys at or before the query bit-equal, the rest left unwritten."""
+    got = got.cpu().numpy().astype(np.int64)
+    low = np.tril(np.ones(got.shape, dtype=bool))
+    bad = np.count_nonzero(got[low] != want[low])
+    assert bad == 0, f"{what}: {bad} mismatching causal scores"
+    assert np.all(got[~low] == UNWRITTEN), f"{what}: entries past the diagonal written"
+
+
+def _eight_wave(B, H, S, D):
+    """Whether prefill_attn_run takes the eight-wave kernel for int16 inputs of this shape."""
+    return D == 128 and B * H * ((S + 255) // 256) >= 256
+
+
 @pytest.mark.parametrize("offs", [None, [3]])
 def test_int16_rotation_bit_exact_all_heads(offs):
     w = synth.WORKLOADS["i16_h32_s2048_d128"]
@@ -159,44 +181,69 @@ def test_int16_rotation_bit_exact_all_heads(offs):
 
 
 def test_int16_scores_bit_exact():
+    """All 32 heads of the 1 x 32 x 2048 x 128 int16 workload, scores stored by
+    the eight-wave two-group kernel that prefill_attn_run launches for it."""
     w = synth.WORKLOADS["i16_h32_s2048_d128"]
-    announce("i16 scores")
+    assert _eight_wave(w.batch, w.n_heads, w.seq_len, w.head_dim)
+    announce("i16 scores, eight-wave kernel")
     q, k, v = synth.make_inputs(w)
     attn = _i16_handle(w)
     try:
         qd, kd = to_dev(q, k)
-        sc = torch.empty((w.batch, w.n_heads, w.seq_len, w.seq_len), dtype=torch.int32, device="cuda")
+        sc = _score_buffer(w.batch, w.n_heads, w.seq_len)
         pa.prefill_attn_debug_scores_i32(attn.handle, w.batch, w.seq_len, qd, kd, None, sc)
-        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
         pos = np.arange(w.seq_len)
         qr = oracle.rope_rotate_i16(q[0].numpy(), pos, w.rope_theta)
         kr = oracle.rope_rotate_i16(k[0].numpy(), pos, w.rope_theta)
         for h in range(w.n_heads):
-            want = oracle.scores_i32(qr[:, h], kr[:, h])
-            got = sc[0, h].cpu().numpy().astype(np.int64)
-            assert np.array_equal(got, want), f"head {h}: {np.count_nonzero(got != want)} mismatches"
+            _assert_causal_scores(sc[0, h], oracle.scores_i32(qr[:, h], kr[:, h]), f"head {h}")
     finally:
         attn.close()
 
 
-def test_int16_scores_ragged_gqa_offsets():
-    w = synth.Workload("i16_small", 2, 4, 2, 150, 64, "i16", 1e4, 77, score_scale=2.0 ** -22 / 8)
-    announce(w.name)
+@pytest.mark.parametrize("D", [64, 128])
+def test_int16_scores_ragged_gqa_offsets(D):
+    """A small ragged GQA shape with offsets: the four-wave kernel's scores."""
+    w = synth.Workload("i16_small", 2, 4, 2, 150, D, "i16", 1e4, 77, score_scale=2.0 ** -22 / 8)
+    assert not _eight_wave(2, 4, 150, D)
+    announce(w.name, D)
     q, k, v = synth.make_inputs(w)
     offs = [0, 40]
-    attn = pa.PrefillAttention(4, 2, 64, 190, 1e4)
+    attn = pa.PrefillAttention(4, 2, D, 190, 1e4)
     try:
         qd, kd = to_dev(q, k)
         od = torch.tensor(offs, dtype=torch.int32, device="cuda")
-        sc = torch.empty((2, 4, 150, 150), dtype=torch.int32, device="cuda")
+        sc = _score_buffer(2, 4, 150)
         pa.prefill_attn_debug_scores_i32(attn.handle, 2, 150, qd, kd, od, sc)
-        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
         for b in range(2):
             pos = np.arange(150) + offs[b]
             qr = oracle.rope_rotate_i16(q[b].numpy(), pos, 1e4)
             kr = oracle.rope_rotate_i16(k[b].numpy(), pos, 1e4)
             for h in range(4):
-                assert np.array_equal(sc[b, h].cpu().numpy().astype(np.int64), oracle.scores_i32(qr[:, h], kr[:, h // 2]))
+                _assert_causal_scores(sc[b, h], oracle.scores_i32(qr[:, h], kr[:, h // 2]), f"b{b} h{h}")
+    finally:
+        attn.close()
+
+
+def test_int16_rotation_bit_exact_four_wave_staging():
+    """The rope export at a shape whose prefill stages with 256 threads."""
+    w = synth.Workload("i16_rope_small", 2, 3, 3, 203, 96, "i16", 1e4, 55)
+    assert not _eight_wave(2, 3, 203, 96)
+    announce(w.name)
+    q, k, v = synth.make_inputs(w)
+    offs = [0, 9]
+    attn = pa.PrefillAttention(3, 3, 96, 212, 1e4)
+    try:
+        xd = k.cuda()
+        xr = torch.empty_like(xd)
+        od = torch.tensor(offs, dtype=torch.int32, device="cuda")
+        pa.prefill_attn_debug_rope_i16(attn.handle, 2, 203, xd, 3, od, xr)
+        assert attn.status() == pa.PA_OK
+        for b in range(2):
+            want = oracle.rope_rotate_i16(k[b].numpy(), np.arange(203) + offs[b], 1e4)
+            assert np.array_equal(xr.cpu()[b].numpy().astype(np.int64), want), b
     finally:
         attn.close()
 
@@ -277,9 +324,9 @@ def test_quantised_scores_bit_exact(case):
     try:
         qd, kd = to_dev(q, k)
         od = None if offs is None else torch.tensor(offs, dtype=torch.int32, device="cuda")
-        sc = torch.empty((B, Hq, S, S), dtype=torch.int32, device="cuda")
+        sc = _score_buffer(B, Hq, S)
         pa.prefill_attn_debug_scores_q16(attn.handle, B, S, qd, kd, od, sc)
-        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
         qc, _ = oracle.quantize_rows_i16(q.float().numpy())
         kc, _ = oracle.quantize_rows_i16(k.float().numpy())
         for b in range(B):
@@ -287,9 +334,31 @@ def test_quantised_scores_bit_exact(case):
             qr = oracle.rope_rotate_i16(qc[b], pos, 1e4)
             kr = oracle.rope_rotate_i16(kc[b], pos, 1e4)
             for h in range(Hq):
-                want = oracle.scores_i32(qr[:, h], kr[:, h // (Hq // Hkv)])
-                got = sc[b, h].cpu().numpy().astype(np.int64)
-                assert np.array_equal(got, want), f"b{b} h{h}: {np.count_nonzero(got != want)} mismatches"
+                _assert_causal_scores(sc[b, h], oracle.scores_i32(qr[:, h], kr[:, h // (Hq // Hkv)]), f"b{b} h{h}")
+    finally:
+        attn.close()
+
+
+def test_quantised_scores_bit_exact_workload():
+    """All 32 heads of the quantised 1 x 32 x 2048 x 128 workload, scores stored
+    by the eight-wave kernel that PA_IN_BF16_Q16 runs at that shape."""
+    w = synth.WORKLOADS["q16_bf16_h32_s2048_d128"]
+    assert _eight_wave(w.batch, w.n_heads, w.seq_len, w.head_dim)
+    announce(w.name, "scores")
+    q, k, v = synth.make_inputs(w)
+    attn = pa.PrefillAttention(w.n_heads, w.n_kv_heads, w.head_dim, w.seq_len, w.rope_theta)
+    try:
+        qd, kd = to_dev(q, k)
+        sc = _score_buffer(1, w.n_heads, w.seq_len)
+        pa.prefill_attn_debug_scores_q16(attn.handle, 1, w.seq_len, qd, kd, None, sc)
+        assert attn.status() == pa.PA_OK
+        qc, _ = oracle.quantize_rows_i16(q.float().numpy())
+        kc, _ = oracle.quantize_rows_i16(k.float().numpy())
+        pos = np.arange(w.seq_len)
+        qr = oracle.rope_rotate_i16(qc[0], pos, w.rope_theta)
+        kr = oracle.rope_rotate_i16(kc[0], pos, w.rope_theta)
+        for h in range(w.n_heads):
+            _assert_causal_scores(sc[0, h], oracle.scores_i32(qr[:, h], kr[:, h]), f"head {h}")
     finally:
         attn.close()
 
