@@ -1,0 +1,141 @@
+"""The page's own validation of the piecewise-linear exp, run for three readings
+of its coefficients.
+
+Page: the 2kiu.com/news/6082051 retelling, §3.3.  It cuts x in [-8, 8] into 16
+segments with one line y = a x + b each, stores a and b as int16 evaluated with
+the Q12.4 multiply, and validates on 100k random inputs against an fp32 golden
+model: 99.2% of the outputs err by less than 0.01, the largest error is 0.043,
+at x = 7.8.  The page prints neither the coefficients nor what an "output" is.
+
+Readings of the line on segment [k, k+1):
+  chord     through (k, e^k) and (k+1, e^(k+1)) -- the oracle's (oracle.pwl_exp);
+  minimax   the line of least maximum relative error; on every unit segment it
+            is the chord times 2 / (2 + d), d the chord's largest relative error
+            (the error then equioscillates between -(1 - c) and +(1 - c));
+  q12.4     the chord's a and b (in global x) rounded to Q12.4 int16, evaluated
+            as the Q12.4 product a x + b, saturating at the int16 range.
+Readings of "output":
+  element   E(x) against fp32 e^x, relative error, x uniform on [-8, 8];
+  softmax   probabilities of a vector of n_vec logits uniform on [-8, 8],
+            exp replaced by E (applied to the logits themselves), against the
+            fp32 softmax; 100k logits in all.
+
+Recorded (seed 0) -- the per-element readings stay far from the page (best
+11.8% within 0.01); the softmax reading with the chord reproduces the page's
+99.2% at 48 logits per vector, with its largest error at the top of the range
+as the page says (0.027 at x = 7.98 against the page's 0.043 at 7.8); the
+minimax line gives exactly the chord's probabilities (a constant factor per
+segment that is the same for every segment cancels in the normalisation); the
+Q12.4 coefficients are far worse (largest error 0.35 at 48 logits).  So the
+oracle keeps the chord: among these readings it is the one the page's figures
+support, and the minimax line could not be told from it.
+
+Run with -s to print the table.
+"""
+
+import math
+
+import numpy as np
+
+import oracle
+
+N_SAMPLES = 100_000
+
+
+def _segments(x):
+    k = np.clip(np.floor(x), -8, 7)
+    return k, x - k
+
+
+def chord(x):
+    k, u = _segments(x)
+    return np.exp(k) * (1.0 + (math.e - 1.0) * u)
+
+
+def _chord_max_rel():
+    u = np.linspace(0.0, 1.0, 200_001)
+    return float(np.max((1.0 + (math.e - 1.0) * u) / np.exp(u) - 1.0))
+
+
+def minimax(x):
+    return chord(x) * (2.0 / (2.0 + _chord_max_rel()))
+
+
+def _q124(v):
+    return np.clip(np.round(np.asarray(v, dtype=np.float64) * 16.0), -32768, 32767) / 16.0
+
+
+def q124(x):
+    k, _ = _segments(x)
+    a = np.exp(k) * (math.e - 1.0)  # y = a x + b on segment k, global x
+    b = np.exp(k) * (1.0 - (math.e - 1.0) * k)
+    return np.maximum(_q124(_q124(a) * _q124(x) + _q124(b)), 0.0)
+
+
+READINGS = {"chord": chord, "minimax": minimax, "q12.4": q124}
+
+
+def element_stats(f, seed=0):
+    x = np.random.default_rng(seed).uniform(-8.0, 8.0, N_SAMPLES)
+    ref = np.exp(x.astype(np.float32)).astype(np.float64)
+    rel = np.abs(f(x) - ref) / ref
+    i = int(rel.argmax())
+    return float(np.mean(rel < 0.01)), float(rel[i]), float(x[i])
+
+
+def softmax_stats(f, n_vec, seed=0):
+    x = np.random.default_rng(seed).uniform(-8.0, 8.0, (N_SAMPLES // n_vec, n_vec))
+    e = f(x)
+    p = e / e.sum(axis=1, keepdims=True)
+    r = np.exp(x.astype(np.float32)).astype(np.float64)
+    r = r / r.sum(axis=1, keepdims=True)
+    err = np.abs(p - r)
+    i = np.unravel_index(int(err.argmax()), err.shape)
+    return float(np.mean(err < 0.01)), float(err[i]), float(x[i])
+
+
+def test_chord_is_the_oracles_line():
+    x = np.random.default_rng(1).uniform(-8.0, 8.0, 10_000)
+    assert np.allclose(chord(x), oracle.pwl_exp(x), rtol=1e-15, atol=0)
+
+
+def test_minimax_line_equioscillates():
+    d = _chord_max_rel()
+    assert abs(d - 0.1312) < 5e-4  # the oracle's analytic chord bound
+    c = 2.0 / (2.0 + d)
+    u = np.linspace(0.0, 1.0, 200_001)
+    rel = c * (1.0 + (math.e - 1.0) * u) / np.exp(u) - 1.0
+    assert abs(rel.max() + rel.min()) < 1e-9  # +-(1 - c): equal and opposite extremes
+    # no nearby line does better (a small grid around it)
+    best = np.max(np.abs(rel))
+    for da in np.linspace(-0.01, 0.01, 9):
+        for db in np.linspace(-0.01, 0.01, 9):
+            trial = ((c * (math.e - 1.0) + da) * u + c + db) / np.exp(u) - 1.0
+            assert np.max(np.abs(trial)) >= best - 1e-12
+
+
+def test_page_validation_three_readings():
+    rows = []
+    for name, f in READINGS.items():
+        frac, mx, at = element_stats(f)
+        rows.append(("element", name, "-", frac, mx, at))
+        for n_vec in (16, 48, 128):
+            frac, mx, at = softmax_stats(f, n_vec)
+            rows.append(("softmax", name, n_vec, frac, mx, at))
+    print("\nreading   line      n_vec  <0.01    max err  at x   (page: 99.2%, 0.043 at 7.8)")
+    for kind, name, n_vec, frac, mx, at in rows:
+        print(f"{kind:9s} {name:9s} {str(n_vec):5s} {100 * frac:6.2f}%  {mx:8.4f}  {at:6.3f}")
+    got = {(k, n, v): (fr, mx, at) for k, n, v, fr, mx, at in rows}
+
+    # per-element readings: far from 99.2% whatever the line
+    assert got[("element", "chord", "-")][0] < 0.05 and abs(got[("element", "chord", "-")][1] - 0.1312) < 1e-3
+    assert got[("element", "minimax", "-")][0] < 0.15 and abs(got[("element", "minimax", "-")][1] - 0.0616) < 1e-3
+    assert got[("element", "q12.4", "-")][1] > 1.0  # Q12.4 cannot hold e^x below 2^-5
+    # softmax reading: the chord reproduces the page's fraction at 48 logits, its
+    # largest error sits at the top of the range
+    frac, mx, at = got[("softmax", "chord", 48)]
+    assert abs(frac - 0.992) < 0.002 and 0.02 < mx < 0.043 and at > 7.5
+    # minimax = chord after normalisation; Q12.4 far worse
+    for n_vec in (16, 48, 128):
+        assert np.allclose(got[("softmax", "minimax", n_vec)], got[("softmax", "chord", n_vec)], rtol=1e-9)
+        assert got[("softmax", "q12.4", n_vec)][1] > 0.1
