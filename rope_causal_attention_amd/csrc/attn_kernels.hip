@@ -261,25 +261,26 @@ struct Bf16QK {
     };
     struct KRegs {
         uint4 raw[kPer];
-        uint4 cs[kPer];  // fp16 (cos, sin) of the chunk's 4 pairs
+        uint4 cs[kPer][2];  // fp32 (cos, sin) of the chunk's 4 pairs
     };
     struct KPtr {
         Rows k;
-        const char* tab;  // fp16 table row of position off[b] (2 D bytes per position)
+        const char* tab;  // fp32 table row of position off[b] (4 D bytes per position)
         int S;
     };
     // Q' and K' are fp16: the guard sees every converted value.
     using Guard = F16Guard;
 
     // Rotate 4 adjacent pairs: x' = x c - y s, y' = x s + y c; times `scale`.
-    __device__ static __forceinline__ uint4 rotate8(const uint4& raw, const uint4& cs, float scale, Guard& g) {
+    __device__ static __forceinline__ uint4 rotate8(const uint4& raw, const float4& cs0, const float4& cs1,
+                                                    float scale, Guard& g) {
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-        const uint32_t t[4] = {cs.x, cs.y, cs.z, cs.w};
+        const float t[8] = {cs0.x, cs0.y, cs0.z, cs0.w, cs1.x, cs1.y, cs1.z, cs1.w};
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float x = bf_lo(w[j]), y = bf_hi(w[j]);
-            const float c = h_lo(t[j]), s = h_hi(t[j]);
+            const float c = t[2 * j], s = t[2 * j + 1];
             const float xr = fmaf(x, c, -y * s), yr = fmaf(x, s, y * c);
             o[j] = pack_h2(xr * scale, yr * scale);
             g.add(o[j]);
@@ -290,7 +291,7 @@ struct Bf16QK {
     template <bool MAPPED>
     __device__ static __forceinline__ KPtr kptr(const RunArgs& a, const Ctx& c) {
         return {kv_rows<MAPPED>(a, c, a.k, D, 2),
-                reinterpret_cast<const char*>(a.rope_h2 + static_cast<size_t>(c.koff) * (D / 2)), c.NK};
+                reinterpret_cast<const char*>(a.rope_f32 + static_cast<size_t>(c.koff) * D), c.NK};
     }
 
     __device__ static __forceinline__ void load_q(const RunArgs& a, const Ctx& c, int qi, float scale, Q& q,
@@ -298,16 +299,18 @@ struct Bf16QK {
         const int lh = (threadIdx.x & 63) >> 5;
         const bool ok = qi < c.S;
         const Rows rq = q_rows(a, c, a.q, D, 2);
-        const char* tab = reinterpret_cast<const char*>(a.rope_h2 + static_cast<size_t>(c.off) * (D / 2));
+        const char* tab = reinterpret_cast<const char*>(a.rope_f32 + static_cast<size_t>(c.off) * D);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             const int d0 = 16 * ks + 8 * lh;
-            uint4 raw = make_uint4(0, 0, 0, 0), cs = raw;
+            uint4 raw = make_uint4(0, 0, 0, 0);
+            float4 cs0 = make_float4(0.f, 0.f, 0.f, 0.f), cs1 = cs0;
             if (ok) {
                 raw = ld16(rq.base, qi * rq.stride + 2 * d0);
-                cs = ld16(tab, (qi * D + d0) * 2);
+                cs0 = ld16f(tab, (qi * D + d0) * 4);
+                cs1 = ld16f(tab, (qi * D + d0) * 4 + 16);
             }
-            q.f[ks] = __builtin_bit_cast(f16x8, rotate8(raw, cs, scale, g));
+            q.f[ks] = __builtin_bit_cast(f16x8, rotate8(raw, cs0, cs1, scale, g));
         }
     }
 
@@ -317,7 +320,7 @@ struct Bf16QK {
     template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
         const char* kb = p.k.template tile_base<MAPPED>(tile);
-        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
+        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int idx = min(static_cast<int>(threadIdx.x % NT) + NT * i, kChunks - 1);
@@ -325,18 +328,19 @@ struct Bf16QK {
             const int ch = idx % (D / 8);
             if (CLAMP) row = min(row, p.S - 1 - tile * BN);
             r.raw[i] = ld16(kb, p.k.template row_off<MAPPED>(tile, row) + 16 * ch);
-            r.cs[i] = ld16(tb, (row * D + 8 * ch) * 2);
+            r.cs[i][0] = ld16(tb, (row * D + 8 * ch) * 4);
+            r.cs[i][1] = ld16(tb, (row * D + 8 * ch) * 4 + 16);
         }
     }
 
-    // K' = RoPE(K) rounded once to fp16 (rot_pack_h2h).
-    __device__ static __forceinline__ uint4 rotate8_k(const uint4& raw, const uint4& cs, Guard& g) {
+    // K' = RoPE(K) rounded once to fp16 (rot_pack_f32).
+    __device__ static __forceinline__ uint4 rotate8_k(const uint4& raw, const uint4 (&cs)[2], Guard& g) {
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-        const uint32_t t[4] = {cs.x, cs.y, cs.z, cs.w};
+        const uint32_t t[8] = {cs[0].x, cs[0].y, cs[0].z, cs[0].w, cs[1].x, cs[1].y, cs[1].z, cs[1].w};
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            o[j] = rot_pack_h2h(bf_lo(w[j]), bf_hi(w[j]), t[j]);
+            o[j] = rot_pack_f32(bf_lo(w[j]), bf_hi(w[j]), __uint_as_float(t[2 * j]), __uint_as_float(t[2 * j + 1]));
             g.add(o[j]);
         }
         return make_uint4(o[0], o[1], o[2], o[3]);
@@ -743,7 +747,7 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
     static constexpr int kGran = D / 32;  // granules of 4 elements per thread
     struct KRegs {
         uint2 raw[kGran];
-        uint2 cs[kGran];  // fp16 (cos, sin) of the granule's 2 pairs
+        uint4 cs[kGran];  // fp32 (cos, sin) of the granule's 2 pairs
     };
     template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
@@ -753,11 +757,11 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
         if (CLAMP) row = min(row, p.S - 1 - tile * BN);
         const char* kb = p.k.template tile_base<MAPPED>(tile);
         const uint32_t ro = p.k.template row_off<MAPPED>(tile, row);
-        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
+        const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
 #pragma unroll
         for (int i = 0; i < kGran; ++i) {
             r.raw[i] = *reinterpret_cast<const uint2*>(kb + ro + 2 * (e0 + 4 * i));
-            r.cs[i] = *reinterpret_cast<const uint2*>(tb + (row * D + e0 + 4 * i) * 2);
+            r.cs[i] = ld16(tb, (row * D + e0 + 4 * i) * 4);
         }
     }
     __device__ static __forceinline__ void commit_k(const KRegs& r, char* lds, typename Base::Guard& g) {
@@ -768,11 +772,12 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
 #pragma unroll
         for (int i = 0; i < kGran; ++i) {
             const uint32_t w[2] = {r.raw[i].x, r.raw[i].y};
-            const uint32_t t[2] = {r.cs[i].x, r.cs[i].y};
+            const uint32_t t[4] = {r.cs[i].x, r.cs[i].y, r.cs[i].z, r.cs[i].w};
             uint32_t o[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                o[j] = rot_pack_h2h(bf_lo(w[j]), bf_hi(w[j]), t[j]);
+                o[j] = rot_pack_f32(bf_lo(w[j]), bf_hi(w[j]), __uint_as_float(t[2 * j]),
+                                    __uint_as_float(t[2 * j + 1]));
                 g.add(o[j]);
             }
             *reinterpret_cast<uint2*>(kl + 4 * i) = make_uint2(o[0], o[1]);

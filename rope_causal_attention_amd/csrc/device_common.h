@@ -80,6 +80,17 @@ struct NoGuard {
     __device__ __forceinline__ bool bad() const { return false; }
 };
 
+// The same rotation from fp32 (cos, sin): (x c - y s, x s + y c), the product
+// y s (and y c) rounded to fp32 and one fused multiply-add rounding once to
+// fp16, as rot_pack_h2h.
+__device__ __forceinline__ uint32_t rot_pack_f32(float x, float y, float c, float s) {
+    const float ys = -y * s, yc = y * c;
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]" : "=v"(r) : "v"(x), "v"(c), "v"(ys));
+    asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]" : "+v"(r) : "v"(x), "v"(s), "v"(yc));
+    return r;
+}
+
 __device__ __forceinline__ float h_lo(uint32_t w) { return static_cast<float>(__builtin_bit_cast(f16x2, w)[0]); }
 __device__ __forceinline__ float h_hi(uint32_t w) { return static_cast<float>(__builtin_bit_cast(f16x2, w)[1]); }
 

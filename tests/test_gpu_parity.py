@@ -14,7 +14,7 @@ import torch
 import oracle
 import rope_causal_attention_amd as pa
 import synth
-from gpu_common import (announce, assert_close, errors, need_gpu, oracle_full, oracle_rows, run_gpu, sample_rows,
+from gpu_common import (announce, assert_close, need_gpu, oracle_full, run_gpu,
                         to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -108,27 +108,19 @@ def test_full_workload_whole_output(name):
     got = run_gpu(w, q, k, v)
     want = oracle_full(w, q, k, v)
     mx, mean = assert_close(got.numpy(), want, w.dtype)
-    announce(name, f"max {mx:.2e} mean {mean:.2e}")
+    announce("margin", name, f"max {mx:.3e} mean {mean:.3e}")
 
 
 @pytest.mark.parametrize("reading", ["independent", "shared"])
 def test_long_prompt_workload(reading):
-    """seq 4096, D 96, per-head scales: 3 whole heads plus rows sampled over all heads."""
+    """seq 4096, D 96, per-head scales: the whole O (all 32 heads) against the oracle."""
     w = synth.workload("mha_bf16_h32_s4096_d96", head_scale=reading)
     announce(w.name, reading)
     q, k, v = synth.make_inputs(w)
     got = run_gpu(w, q, k, v).numpy()
-    worst = []
-    for h in (0, 17, 31):
-        one = synth.workload("mha_bf16_h32_s4096_d96", n_heads=1, n_kv_heads=1)
-        want = oracle_full(one, q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1])
-        worst.append(assert_close(got[:, :, h:h + 1], want, "bf16"))
-    rows = sample_rows(w, 96, seed=7)
-    want = oracle_rows(w, q, k, v, rows)
-    sel = np.stack([got[b, i, h] for b, h, i in rows])
-    mx, _ = errors(sel, want)
-    assert mx <= 1e-2, f"sampled rows max-abs {mx:.3e}"
-    announce(w.name, reading, "heads", [f"{a:.2e}/{b:.2e}" for a, b in worst], f"rows max {mx:.2e}")
+    want = oracle_full(w, q, k, v)
+    mx, mean = assert_close(got, want, "bf16")
+    announce("margin", w.name, reading, f"max {mx:.3e} mean {mean:.3e}")
 
 
 # ------------------------------------------------------------ int16 variant
@@ -249,19 +241,13 @@ def test_int16_rotation_bit_exact_four_wave_staging():
 
 
 def test_int16_attention_output():
+    """1 x 32 x 2048 x 128 int16: the whole O against the oracle."""
     w = synth.WORKLOADS["i16_h32_s2048_d128"]
     announce(w.name)
     q, k, v = synth.make_inputs(w)
     got = run_gpu(w, q, k, v).numpy()
-    for h in (0, 31):
-        one = synth.workload(w.name, n_heads=1, n_kv_heads=1)
-        want = oracle_full(one, q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1])
-        assert_close(got[:, :, h:h + 1], want, "bf16")
-    rows = sample_rows(w, 64, seed=9)
-    want = oracle_rows(w, q, k, v, rows)
-    sel = np.stack([got[b, i, h] for b, h, i in rows])
-    mx, _ = errors(sel, want)
-    assert mx <= 1e-2
+    mx, mean = assert_close(got, oracle_full(w, q, k, v), "bf16")
+    announce("margin", w.name, f"max {mx:.3e} mean {mean:.3e}")
 
 
 # Plain head_dim 128 launches with at least 256 workgroups of 256 query rows
@@ -384,21 +370,13 @@ def test_quantised_attention_small_full_compare(case):
 
 
 def test_quantised_attention_workload():
-    """1 x 32 x 2048 x 128 bf16 through the in-kernel quantisation: two whole heads
-    and rows sampled over all heads."""
+    """1 x 32 x 2048 x 128 bf16 through the in-kernel quantisation: the whole O."""
     w = synth.WORKLOADS["q16_bf16_h32_s2048_d128"]
     announce(w.name)
     q, k, v = synth.make_inputs(w)
     got = run_gpu(w, q, k, v).numpy()
-    for h in (0, 31):
-        one = synth.workload(w.name, n_heads=1, n_kv_heads=1)
-        want = oracle_full(one, q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1])
-        assert_close(got[:, :, h:h + 1], want, "bf16")
-    rows = sample_rows(w, 64, seed=13)
-    want = oracle_rows(w, q, k, v, rows)
-    sel = np.stack([got[b, i, h] for b, h, i in rows])
-    mx, _ = errors(sel, want)
-    assert mx <= 1e-2
+    mx, mean = assert_close(got, oracle_full(w, q, k, v), "bf16")
+    announce("margin", w.name, f"max {mx:.3e} mean {mean:.3e}")
 
 
 def test_quantised_cached_equals_quantised_prefill_bitwise():

@@ -35,6 +35,33 @@ def test_first_row_is_first_value_row_bitwise(dt):
         assert torch.equal(o[:, 0, h], v[:, 0, h // g].float())
 
 
+# V = I (S <= D): O is the probability matrix itself.  Four-wave and eight-wave shapes.
+IDENTITY_SHAPES = [("4wave", 1, 4, 2), ("8wave", 2, 128, 128)]
+
+
+@pytest.mark.parametrize("shape", IDENTITY_SHAPES, ids=[s[0] for s in IDENTITY_SHAPES])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "i16"])
+def test_identity_values_give_the_probabilities(dt, shape):
+    """V = I makes O[i, j] = P[i, j]: entries past the diagonal exactly 0
+    (masked keys weigh exactly nothing), rows summing to 1, and the
+    probabilities equal to the oracle's (the oracle with V = I)."""
+    name, B, Hq, Hkv = shape
+    S, D = 96, 128
+    announce("v=I", dt, name)
+    w = _w(dt, B=B, Hq=Hq, Hkv=Hkv, S=S, D=D)
+    q, k, v = synth.make_inputs(w)
+    eye = torch.zeros(S, D)
+    eye[:, :S] = torch.eye(S)
+    v = eye[None, :, None, :].expand(B, S, Hkv, D).contiguous().to(v.dtype)
+    o = run_gpu(w, q, k, v)
+    p = o[..., :S].double()  # [B][S][Hq][S]
+    upper = torch.triu(torch.ones(S, S, dtype=torch.bool), diagonal=1)
+    assert torch.all(p.permute(0, 2, 1, 3)[:, :, upper] == 0)
+    assert torch.all(o[..., S:] == 0)
+    assert float((p.sum(-1) - 1).abs().max()) <= 1e-5
+    assert_close(o.numpy(), oracle_full(w, q, k, v), "f32" if dt == "f32" else "bf16")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16", "i16"])
 def test_constant_values_give_constant_output(dt):
     announce("v=1", dt)
