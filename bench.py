@@ -37,6 +37,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused RoPE causal prefill attention: tokens/s and TFLOP/s (% bf16 MFMA peak)"
 PEAK_TFLOPS = 2516.6       # MI355X dense fp16/bf16 matrix-core peak (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+BALANCE = PEAK_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte where the two bounds meet
 DEFAULT_WORKLOAD = "mha_bf16_h32_s4096_d96"
 KERNEL_SOURCE = os.path.join(ROOT, "rope_causal_attention_amd", "csrc", "attn_kernels.hip")
 
@@ -56,7 +58,8 @@ def algorithmic_bytes(w):
     q = w.batch * w.seq_len * w.n_heads * w.head_dim * el
     kv = 2 * w.batch * w.seq_len * w.n_kv_heads * w.head_dim * (el if w.dtype != "i16" else 2)
     o = w.batch * w.seq_len * w.n_heads * w.head_dim * 4
-    tab = w.seq_len * w.head_dim * (4 if w.dtype == "f32" else 2)  # fp32, or fp16 / Q1.14 pairs
+    # (cos, sin) pairs per position: fp32 for the float paths, Q1.14 int16 for the integer ones
+    tab = w.seq_len * w.head_dim * (4 if w.dtype in ("f32", "bf16") else 2)
     return q + kv + o + tab
 
 
@@ -194,7 +197,9 @@ def bench_decode(args, torch, pa):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=70)
+    ap.add_argument("--samples", type=int, default=7,
+                    help="the timed steps are split into this many equal samples; the median sample is reported")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -267,20 +272,34 @@ def main():
     if args.calib_copy:
         calib_copy(torch)
 
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # Measured roofline denominators (matrix-core peak, shader clock).
+    peak_meas, clock_ghz = max(pa.prefill_attn_device_peak(stream) for _ in range(2))
+    log(f"measured matrix-core peak {peak_meas:.0f} TFLOP/s at {clock_ghz:.3f} GHz "
+        f"(vendor {PEAK_TFLOPS} at 2.4 GHz)")
+
+    # The timed steps in equal samples, each bracketed by events on the launch
+    # stream; the median sample is the figure (the clock and the temperature
+    # move between samples).
+    n_samples = max(1, min(args.samples, args.steps))
+    per = args.steps // n_samples
+    sizes = [per + (1 if i < args.steps % n_samples else 0) for i in range(n_samples)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_samples + 1)]
     torch.cuda.synchronize()
     t_host0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
+    marks[0].record(stream)
+    for i, n in enumerate(sizes):
+        for _ in range(n):
+            step()
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host0
     if attn.status() != pa.PA_OK:
         raise RuntimeError("status word set during the timed steps")
-    ms = e0.elapsed_time(e1) / args.steps
-    log(f"{w.name} [{args.mode}]: {ms * 1e3:.1f} us/step (host wall {t_host / args.steps * 1e6:.1f} us/step)")
+    sample_ms = sorted(marks[i].elapsed_time(marks[i + 1]) / sizes[i] for i in range(n_samples))
+    ms = sample_ms[len(sample_ms) // 2]
+    log(f"{w.name} [{args.mode}]: median {ms * 1e3:.1f} us/step over {n_samples} samples "
+        f"(min {sample_ms[0] * 1e3:.1f}, max {sample_ms[-1] * 1e3:.1f}; "
+        f"host wall {t_host / args.steps * 1e6:.1f} us/step)")
 
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -299,10 +318,21 @@ def main():
         step()
         a1.record(stream)
     torch.cuda.synchronize()
-    launch_ms = sum(a0.elapsed_time(a1) for a0, a1 in pairs) / len(pairs)
+    launch_all = sorted(a0.elapsed_time(a1) for a0, a1 in pairs)
+    launch_ms = launch_all[len(launch_all) // 2]
     launch_tflops = flops / (launch_ms * 1e-3) / 1e12
-    log(f"per launch: {launch_ms * 1e3:.1f} us = {launch_tflops:.1f} TFLOP/s "
-        f"({100 * launch_tflops / PEAK_TFLOPS:.1f}% of {PEAK_TFLOPS})")
+    log(f"per launch (median of {len(launch_all)}): {launch_ms * 1e3:.1f} us = {launch_tflops:.1f} TFLOP/s "
+        f"({100 * launch_tflops / PEAK_TFLOPS:.1f}% of {PEAK_TFLOPS}, "
+        f"{100 * launch_tflops / peak_meas:.1f}% of the measured {peak_meas:.0f})")
+    algo = algorithmic_bytes(w)
+    hbm_bound = args.mode == "prefill" and flops / algo < BALANCE
+    if hbm_bound:
+        gbs = algo / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}
+        log(f"HBM-bound workload ({flops / algo:.0f} FLOP/B < {BALANCE:.0f}): {gbs:.0f} GB/s")
+    else:
+        roof = {"bound": "mfma", "achieved": launch_tflops, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": launch_tflops / PEAK_TFLOPS}
 
     cpu = None
     if not args.no_cpu_baseline and args.mode == "prefill":
@@ -338,16 +368,16 @@ def main():
             "tflops": tflops,
             "pct_bf16_peak": 100 * tflops / PEAK_TFLOPS,
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": launch_tflops,
-            "peak": PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": launch_tflops / PEAK_TFLOPS,
+        "roofline": dict(roof, **{
             "launch_us": launch_ms * 1e3,
             "traffic": traffic_record(w) if args.mode == "prefill" else None,
-            "algorithmic_bytes": algorithmic_bytes(w),
-        },
+            "algorithmic_bytes": algo,
+            "flop": flops,
+            "measured_mfma_peak_tflops": peak_meas,
+            "shader_clock_ghz": clock_ghz,
+            "frac_of_measured_peak": launch_tflops / peak_meas if peak_meas else None,
+            "samples_us": [round(x * 1e3, 2) for x in sample_ms],
+        }),
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -259,6 +259,19 @@ int prefill_attn_decode_noalloc(const prefill_attn* h, int in_dtype, int batch, 
 size_t prefill_attn_decode_noalloc_scratch_bytes(void);
 
 /*
+ * Device characterisation (not part of the attention path): the measured
+ * matrix-core peak of the current device in TFLOP/s (v_mfma_f32_32x32x16_f16
+ * on every CU, four independent accumulators per wave, two waves per SIMD,
+ * operands varying lane by lane, over a launch of about 10 ms) and the shader
+ * clock it held in GHz (shader-clock over real-time counter),
+ * the roofline denominators reported beside the vendor peak (the XNet-DNN
+ * article, §三: kernels measured against a micro-benchmarked roofline).
+ * Synchronous; allocates and frees a few KB of device memory; under a second.
+ * PA_EDEVICE if the current device is not gfx950.
+ */
+int prefill_attn_device_peak(double* tflops, double* clock_ghz, void* stream);
+
+/*
  * Host-only index-map builders (caller-owned host arrays; copy the result to the
  * device row of the sequence).
  *   prefill_attn_ring_map:  map[j] = (start + j) mod n_slots, j < count (a ring of

@@ -28,7 +28,7 @@ __all__ = [
     "prefill_attn_debug_rope_i16", "prefill_attn_debug_scores_i32", "prefill_attn_debug_scores_q16",
     "prefill_attn_kv_cache_update", "prefill_attn_run_cached", "prefill_attn_ring_map", "prefill_attn_paged_map",
     "prefill_attn_decode", "prefill_attn_decode_workspace_size",
-    "prefill_attn_decode_noalloc", "prefill_attn_decode_noalloc_scratch_bytes",
+    "prefill_attn_decode_noalloc", "prefill_attn_decode_noalloc_scratch_bytes", "prefill_attn_device_peak",
     "prefill_attn_run_cached_splitk", "prefill_attn_run_cached_workspace_size",
     "PrefillAttention", "EXPORTED_SYMBOLS",
 ]
@@ -66,6 +66,7 @@ _SIGNATURES = {
                                  ctypes.c_size_t, _P]),
     "prefill_attn_decode_noalloc": (_I, [_P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _I, _P]),
     "prefill_attn_decode_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "prefill_attn_device_peak": (_I, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -296,6 +297,14 @@ def prefill_attn_decode_noalloc(handle, in_dtype, batch, q, k_cache, v_cache, n_
 def prefill_attn_decode_noalloc_scratch_bytes():
     """Bytes of the fixed scratch that prefill_attn_decode_noalloc's partials use."""
     return int(load_library().prefill_attn_decode_noalloc_scratch_bytes())
+
+
+def prefill_attn_device_peak(stream=None):
+    """(measured matrix-core TFLOP/s, shader clock GHz) of the current device."""
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    _check(load_library().prefill_attn_device_peak(ctypes.byref(tf), ctypes.byref(ghz), _stream(stream)),
+           "prefill_attn_device_peak")
+    return tf.value, ghz.value
 
 
 # ------------------------------------------------------------- tensor helper

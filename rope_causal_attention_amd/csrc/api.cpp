@@ -408,6 +408,18 @@ extern "C" int prefill_attn_decode_noalloc(const prefill_attn* h, int in_dtype, 
 
 extern "C" size_t prefill_attn_decode_noalloc_scratch_bytes(void) { return pa::kNoAllocScratchBytes; }
 
+extern "C" int prefill_attn_device_peak(double* tflops, double* clock_ghz, void* stream) {
+    if (!tflops || !clock_ghz) return PA_EINVAL;
+    *tflops = 0.0;
+    *clock_ghz = 0.0;
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return PA_EDEVICE;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return PA_EDEVICE;
+    const hipError_t e = pa::measure_device_peak(60000, tflops, clock_ghz, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
 extern "C" int prefill_attn_ring_map(int n_slots, int start, int count, int32_t* map) {
     if (n_slots < 1 || start < 0 || start >= n_slots || count < 0 || (count > 0 && !map)) return PA_EINVAL;
     for (int j = 0; j < count; ++j) map[j] = static_cast<int32_t>((static_cast<long long>(start) + j) % n_slots);

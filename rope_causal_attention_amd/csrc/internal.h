@@ -104,6 +104,11 @@ constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
 // runs once per device (init, or the first call on another device).
 hipError_t noalloc_scratch(float** ptr);
 
+// Matrix-core peak (TFLOP/s of v_mfma_f32_32x32x16_f16, every CU busy) and the
+// shader clock of the current device, measured by one timed launch of `iters`
+// loop steps (allocates and synchronises: a characterisation call).
+hipError_t measure_device_peak(int iters, double* tflops, double* clock_ghz, hipStream_t stream);
+
 // Int16 test exports; RunArgs.q is the tensor to rotate (x) for the rope one,
 // q/k for the scores one; `dst` receives int16 x_rot or int32 scores.
 hipError_t launch_debug_rope_i16(int head_dim, const RunArgs& a, int n_heads_x, int16_t* dst,

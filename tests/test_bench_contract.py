@@ -46,9 +46,19 @@ def test_long_prompt_roofline_inputs():
     assert (B, S, H, Hkv, D, w.dtype) == (1, 4096, 32, 32, 96, "bf16")
     # Causal pairs S(S+1)/2 per head, 2 matmuls x 2 FLOP per multiply-add.
     assert w.flops() == 4 * B * H * D * (S * (S + 1) // 2) == 103_104_380_928
-    # Q, K, V bf16 read once + O fp32 written once + one fp16 (cos, sin) table row per position.
-    assert bench.algorithmic_bytes(w) == 3 * S * H * D * 2 + S * H * D * 4 + S * D * 2 == 126_615_552
+    # Q, K, V bf16 read once + O fp32 written once + one fp32 (cos, sin) table row per position.
+    assert bench.algorithmic_bytes(w) == 3 * S * H * D * 2 + S * H * D * 4 + S * D * 4 == 127_401_984
     assert bench.PEAK_TFLOPS == 2516.6
+    # matrix-bound: its FLOP per algorithmic byte is above the machine balance
+    assert w.flops() / bench.algorithmic_bytes(w) > bench.BALANCE
+
+
+def test_short_prompts_are_hbm_bound():
+    """The 512-token prompts sit below the balance point: the bench reports them in GB/s."""
+    for name in ("mha_bf16_h32_s512_d128", "gqa_bf16_b16_h16kv8_s512_d128"):
+        w = synth.WORKLOADS[name]
+        assert w.flops() / bench.algorithmic_bytes(w) < bench.BALANCE, name
+    assert abs(bench.BALANCE - 2516.6e12 / 8000e9) < 1e-9
 
 
 def test_traffic_record_only_for_the_current_kernel_source(monkeypatch):
@@ -91,4 +101,9 @@ def test_bench_prints_one_contract_line():
     assert 0 < rf["launch_us"] <= 1.25e3 * d["ms_per_step"]  # a sanity bound: 3 launches, a cold box
     assert abs(rf["achieved"] - w.flops() / (rf["launch_us"] * 1e-6) / 1e12) <= 1e-6 * rf["achieved"]
     assert rf["traffic"] is None or rf["traffic"] > 0
+    # measured denominators beside the vendor peak: the matrix-core rate the
+    # chip holds and its shader clock
+    assert 200 < rf["measured_mfma_peak_tflops"] < 1.2 * bench.PEAK_TFLOPS
+    assert 0.3 < rf["shader_clock_ghz"] < 3.0
+    assert len(rf["samples_us"]) == 3 and rf["samples_us"] == sorted(rf["samples_us"])
     assert d["cpu_baseline"] is None  # --no-cpu-baseline
