@@ -12,11 +12,12 @@ with per-head scales, RoPE theta 1e4, causal).  Prints one JSON line.
                     [--mode prefill|chunked|decode] [--chunk N]
 
 --mode chunked prefills the same prompt in chunks of N tokens through a KV
-cache (a ring of seq_len slots): each chunk's K/V is copied into the cache
-(prefill_attn_kv_cache_update), then its queries attend to every cached key
-(prefill_attn_run_cached_splitk, which splits the cached keys over several
-workgroups; --no-split runs prefill_attn_run_cached).  A step is the whole
-prompt, all chunks.
+cache (a ring of seq_len slots): each chunk's K/V is written to the cache and
+its queries attend to every cached key in one launch
+(prefill_attn_run_cached_update, which splits the cached keys over several
+workgroups; --no-split keeps one workgroup per query block;
+--separate-update runs prefill_attn_kv_cache_update, then
+prefill_attn_run_cached_splitk).  A step is the whole prompt, all chunks.
 
 --mode decode times decode attention (prefill_attn_decode): 16 sequences each
 with one new token at position 4095 against a paged bf16 KV cache of 4096
@@ -214,6 +215,9 @@ def main():
                     help="split count for --mode chunked / decode (0 = chosen by the library)")
     ap.add_argument("--no-split", dest="split", action="store_false",
                     help="--mode chunked without split-K over the cached keys")
+    ap.add_argument("--separate-update", dest="fuse", action="store_false",
+                    help="--mode chunked with the cache update as its own launch (kv_cache_update, then "
+                         "run_cached) instead of prefill_attn_run_cached_update")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -258,6 +262,11 @@ def main():
 
         def step():
             for (off, qc, kn, vn), oc in zip(pieces, outs):
+                if args.fuse:
+                    attn.run_cached_update(qc, kn, vn, kc, vc, kv_map, pos_offsets=off, score_scale=w.score_scale,
+                                           out=oc, stream=stream, n_split=args.n_split if args.split else 1,
+                                           workspace=ws if args.split else None)
+                    continue
                 attn.kv_cache_update(kn, vn, kc, vc, kv_map, off, stream=stream)
                 attn.run_cached(qc, kc, vc, kv_map, pos_offsets=off, score_scale=w.score_scale, out=oc,
                                 stream=stream, n_split=args.n_split if args.split else 1,
@@ -354,7 +363,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name if args.mode == "prefill" else
-            f"{w.name}, chunked prefill in chunks of {args.chunk}" + ("" if args.split else ", no split-K"),
+            f"{w.name}, chunked prefill in chunks of {args.chunk}" + ("" if args.split else ", no split-K")
+            + ("" if args.fuse else ", separate cache update"),
             "mode": args.mode,
             "softmax": "piecewise-linear" if args.pwl_softmax else "exp",
             "batch": w.batch,

@@ -199,6 +199,31 @@ int prefill_attn_run_cached_splitk(const prefill_attn* h, int in_dtype, int batc
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * prefill_attn_run_cached_update: prefill_attn_kv_cache_update followed by
+ * prefill_attn_run_cached_splitk (n_split, workspace and their rules as
+ * there; n_split = 1 is the unsplit prefill_attn_run_cached), as one launch
+ * for the 16-bit input types: the attention reads the chunk's own keys
+ * (logical positions pos_offsets[b] .. pos_offsets[b] + seq_len - 1) from
+ * k_new / v_new ([batch][seq_len][n_kv_heads][head_dim], as for the update),
+ * and the same launch writes those rows to their cache slots.  The update's
+ * copy then costs no launch of its own and its rows are read once (the page
+ * titled "手写内核实现6倍prefill加速", §2.2 and §3.2: the update copies only
+ * the new tokens into the KV cache the attention reads through the index map).
+ * Precondition beyond the update's: no slot that the chunk writes is the slot
+ * of another logical position the chunk's queries attend to (the map is
+ * one-to-one over positions 0 .. pos_offsets[b] + seq_len - 1).  Results equal
+ * those of the two calls bit for bit; a chunk whose positions leave the table
+ * or the map writes nothing and gets O = 0 (PA_ERANGE).  PA_IN_F32 runs the two
+ * calls as two launches.
+ */
+int prefill_attn_run_cached_update(const prefill_attn* h, int in_dtype, int batch, int seq_len,
+                                   const void* q, const void* k_new, const void* v_new,
+                                   void* k_cache, void* v_cache, int n_slots,
+                                   const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
+                                   float* out, float score_scale, int n_split,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode attention: one new token per sequence against the KV cache.
  *
  * Sources: the page titled "手写内核实现6倍prefill加速", §3.1 (RoPE from

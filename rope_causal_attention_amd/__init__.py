@@ -29,7 +29,7 @@ __all__ = [
     "prefill_attn_kv_cache_update", "prefill_attn_run_cached", "prefill_attn_ring_map", "prefill_attn_paged_map",
     "prefill_attn_decode", "prefill_attn_decode_workspace_size",
     "prefill_attn_decode_noalloc", "prefill_attn_decode_noalloc_scratch_bytes", "prefill_attn_device_peak",
-    "prefill_attn_run_cached_splitk", "prefill_attn_run_cached_workspace_size",
+    "prefill_attn_run_cached_splitk", "prefill_attn_run_cached_workspace_size", "prefill_attn_run_cached_update",
     "PrefillAttention", "EXPORTED_SYMBOLS",
 ]
 
@@ -64,6 +64,8 @@ _SIGNATURES = {
                                             _P, ctypes.c_size_t, _P]),
     "prefill_attn_decode": (_I, [_P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _I, _P,
                                  ctypes.c_size_t, _P]),
+    "prefill_attn_run_cached_update": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float,
+                                            _I, _P, ctypes.c_size_t, _P]),
     "prefill_attn_decode_noalloc": (_I, [_P, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, ctypes.c_float, _I, _P]),
     "prefill_attn_decode_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "prefill_attn_device_peak": (_I, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), _P]),
@@ -269,6 +271,18 @@ def prefill_attn_run_cached_splitk(handle, in_dtype, batch, seq_len, q, k_cache,
            "prefill_attn_run_cached_splitk")
 
 
+def prefill_attn_run_cached_update(handle, in_dtype, batch, seq_len, q, k_new, v_new, k_cache, v_cache, n_slots,
+                                   kv_map, map_stride, pos_offsets, out, score_scale=0.0, n_split=1, workspace=None,
+                                   workspace_bytes=0, stream=None):
+    """Enqueue the cache update of a chunk and its cached prefill in one launch (see the header)."""
+    _check(load_library().prefill_attn_run_cached_update(handle, in_dtype, batch, seq_len, _ptr(q), _ptr(k_new),
+                                                         _ptr(v_new), _ptr(k_cache), _ptr(v_cache), n_slots,
+                                                         _ptr(kv_map), map_stride, _ptr(pos_offsets), _ptr(out),
+                                                         float(score_scale), n_split, _ptr(workspace),
+                                                         int(workspace_bytes), _stream(stream)),
+           "prefill_attn_run_cached_update")
+
+
 def prefill_attn_decode_workspace_size(handle, batch, n_split):
     """Bytes of workspace a decode call with n_split > 1 needs (0 for n_split = 1)."""
     return int(load_library().prefill_attn_decode_workspace_size(handle, batch, n_split))
@@ -440,6 +454,31 @@ class PrefillAttention:
             ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
             prefill_attn_run_cached_splitk(self.handle, dt, B, S, q, k_cache, v_cache, n_slots, kv_map, stride,
                                            pos_offsets, out, score_scale, n_split, workspace, ws_bytes, stream)
+        return out
+
+    def run_cached_update(self, q, k_new, v_new, k_cache, v_cache, kv_map, pos_offsets=None, score_scale=0.0,
+                          out=None, stream=None, quantize=False, n_split=1, workspace=None):
+        """kv_cache_update of the chunk's k_new/v_new followed by run_cached, as one
+        launch (prefill_attn_run_cached_update).  Returns O (float32)."""
+        dt = self._dtype(q, quantize)
+        B, S, Hq, D = q.shape
+        if Hq != self.n_heads or D != self.head_dim or not q.is_cuda or not q.is_contiguous():
+            raise ValueError("q must be a contiguous device tensor [B][S][n_heads][head_dim]")
+        if tuple(k_new.shape) != (B, S, self.n_kv_heads, self.head_dim) or v_new.shape != k_new.shape:
+            raise ValueError("k_new/v_new must be [B][S][n_kv_heads][head_dim]")
+        if not (k_new.is_contiguous() and v_new.is_contiguous()):
+            raise ValueError("k_new/v_new must be contiguous")
+        n_slots, stride = self._check_cache(k_cache, v_cache, kv_map, dt, B)
+        if pos_offsets is not None and (pos_offsets.dtype != torch.int32 or pos_offsets.numel() != B
+                                        or not pos_offsets.is_cuda):
+            raise ValueError("pos_offsets must be a device int32 tensor with one entry per batch element")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        elif out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+            raise ValueError("out must be contiguous float32 [B][S][n_heads][head_dim]")
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        prefill_attn_run_cached_update(self.handle, dt, B, S, q, k_new, v_new, k_cache, v_cache, n_slots, kv_map,
+                                       stride, pos_offsets, out, score_scale, n_split, workspace, ws_bytes, stream)
         return out
 
     def decode(self, q, k_cache, v_cache, kv_map, pos_offsets=None, score_scale=0.0, n_split=0, workspace=None,

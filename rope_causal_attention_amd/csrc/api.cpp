@@ -204,10 +204,13 @@ extern "C" int prefill_attn_kv_cache_update(const prefill_attn* h, int in_dtype,
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
-extern "C" int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int batch, int seq_len, const void* q,
-                                       const void* k_cache, const void* v_cache, int n_slots, const int32_t* kv_map,
-                                       int map_stride, const int32_t* pos_offsets, float* out, float score_scale,
-                                       void* stream) {
+namespace {
+
+// run_cached, optionally with the chunk's own K/V (k_new, v_new: read by the
+// attention for the chunk's keys and written to the cache by the same launch).
+int run_cached_impl(const prefill_attn* h, int in_dtype, int batch, int seq_len, const void* q, const void* k_new,
+                    const void* v_new, const void* k_cache, const void* v_cache, int n_slots, const int32_t* kv_map,
+                    int map_stride, const int32_t* pos_offsets, float* out, float score_scale, void* stream) {
     pa::RunArgs a;
     int rc = prepare(h, batch, seq_len, pos_offsets, a);
     if (rc != PA_OK) return rc;
@@ -217,9 +220,12 @@ extern "C" int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int 
     rc = check_cache(h, el, seq_len, n_slots, kv_map, map_stride, k_cache, v_cache);
     if (rc != PA_OK) return rc;
     if (!q || !out || !aligned16(q) || !aligned16(out)) return PA_EINVAL;
+    if (k_new && (!aligned16(k_new) || !v_new || !aligned16(v_new))) return PA_EINVAL;
     a.q = q;
     a.k = k_cache;
     a.v = v_cache;
+    a.k_new = k_new;
+    a.v_new = v_new;
     a.out = out;
     a.kv_map = kv_map;
     a.map_stride = map_stride;
@@ -236,6 +242,16 @@ extern "C" int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int 
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
+}  // namespace
+
+extern "C" int prefill_attn_run_cached(const prefill_attn* h, int in_dtype, int batch, int seq_len, const void* q,
+                                       const void* k_cache, const void* v_cache, int n_slots, const int32_t* kv_map,
+                                       int map_stride, const int32_t* pos_offsets, float* out, float score_scale,
+                                       void* stream) {
+    return run_cached_impl(h, in_dtype, batch, seq_len, q, nullptr, nullptr, k_cache, v_cache, n_slots, kv_map,
+                           map_stride, pos_offsets, out, score_scale, stream);
+}
+
 namespace {
 
 size_t split_ws_bytes(const prefill_attn* h, int batch, int seq_len, int n_split) {
@@ -250,11 +266,12 @@ extern "C" size_t prefill_attn_run_cached_workspace_size(const prefill_attn* h, 
     return n_split == 1 ? 0 : split_ws_bytes(h, batch, seq_len, n_split);
 }
 
-extern "C" int prefill_attn_run_cached_splitk(const prefill_attn* h, int in_dtype, int batch, int seq_len,
-                                              const void* q, const void* k_cache, const void* v_cache, int n_slots,
-                                              const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
-                                              float* out, float score_scale, int n_split, void* workspace,
-                                              size_t workspace_bytes, void* stream) {
+namespace {
+
+int splitk_impl(const prefill_attn* h, int in_dtype, int batch, int seq_len, const void* q, const void* k_new,
+                const void* v_new, const void* k_cache, const void* v_cache, int n_slots, const int32_t* kv_map,
+                int map_stride, const int32_t* pos_offsets, float* out, float score_scale, int n_split,
+                void* workspace, size_t workspace_bytes, void* stream) {
     if (!h || n_split < 0) return PA_EINVAL;
     if (workspace && !aligned16(workspace)) return PA_EINVAL;
     if (in_dtype == PA_IN_F32 || batch <= 0 || seq_len <= 0) n_split = 1;  // fp32 kernel has no split
@@ -270,8 +287,8 @@ extern "C" int prefill_attn_run_cached_splitk(const prefill_attn* h, int in_dtyp
     if (n_split > 1 && (!workspace || workspace_bytes < split_ws_bytes(h, batch, seq_len, 2))) n_split = 1;
     while (n_split > 1 && split_ws_bytes(h, batch, seq_len, n_split) > workspace_bytes) --n_split;
     if (n_split == 1)
-        return prefill_attn_run_cached(h, in_dtype, batch, seq_len, q, k_cache, v_cache, n_slots, kv_map,
-                                       map_stride, pos_offsets, out, score_scale, stream);
+        return run_cached_impl(h, in_dtype, batch, seq_len, q, k_new, v_new, k_cache, v_cache, n_slots, kv_map,
+                               map_stride, pos_offsets, out, score_scale, stream);
 
     pa::RunArgs a;
     int rc = prepare(h, batch, seq_len, pos_offsets, a);
@@ -281,11 +298,14 @@ extern "C" int prefill_attn_run_cached_splitk(const prefill_attn* h, int in_dtyp
     rc = check_cache(h, el, seq_len, n_slots, kv_map, map_stride, k_cache, v_cache);
     if (rc != PA_OK) return rc;
     if (!q || !out || !aligned16(q) || !aligned16(out)) return PA_EINVAL;
+    if (k_new && (!aligned16(k_new) || !v_new || !aligned16(v_new))) return PA_EINVAL;
     const long long grid = ((static_cast<long long>(seq_len) + 127) / 128) * batch * h->n_heads * n_split;
     if (grid > 0x7fffffffLL) return PA_EINVAL;
     a.q = q;
     a.k = k_cache;
     a.v = v_cache;
+    a.k_new = k_new;
+    a.v_new = v_new;
     a.out = out;
     a.kv_map = kv_map;
     a.map_stride = map_stride;
@@ -310,6 +330,36 @@ extern "C" int prefill_attn_run_cached_splitk(const prefill_attn* h, int in_dtyp
     m.n_split = n_split;
     e = pa::launch_split_merge(h->head_dim, m, s);
     return e == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" int prefill_attn_run_cached_splitk(const prefill_attn* h, int in_dtype, int batch, int seq_len,
+                                              const void* q, const void* k_cache, const void* v_cache, int n_slots,
+                                              const int32_t* kv_map, int map_stride, const int32_t* pos_offsets,
+                                              float* out, float score_scale, int n_split, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+    return splitk_impl(h, in_dtype, batch, seq_len, q, nullptr, nullptr, k_cache, v_cache, n_slots, kv_map,
+                       map_stride, pos_offsets, out, score_scale, n_split, workspace, workspace_bytes, stream);
+}
+
+extern "C" int prefill_attn_run_cached_update(const prefill_attn* h, int in_dtype, int batch, int seq_len,
+                                              const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                              void* v_cache, int n_slots, const int32_t* kv_map, int map_stride,
+                                              const int32_t* pos_offsets, float* out, float score_scale, int n_split,
+                                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (!h) return PA_EINVAL;
+    if (!k_new || !v_new) return PA_EINVAL;
+    if (in_dtype == PA_IN_F32) {
+        // the fp32 kernel reads every key from the cache: the update runs first
+        const int rc = prefill_attn_kv_cache_update(h, in_dtype, batch, seq_len, k_new, v_new, pos_offsets, kv_map,
+                                                    map_stride, k_cache, v_cache, n_slots, stream);
+        if (rc != PA_OK) return rc;
+        return prefill_attn_run_cached(h, in_dtype, batch, seq_len, q, k_cache, v_cache, n_slots, kv_map, map_stride,
+                                       pos_offsets, out, score_scale, stream);
+    }
+    return splitk_impl(h, in_dtype, batch, seq_len, q, k_new, v_new, k_cache, v_cache, n_slots, kv_map, map_stride,
+                       pos_offsets, out, score_scale, n_split, workspace, workspace_bytes, stream);
 }
 
 namespace {

@@ -112,6 +112,10 @@ struct Rows {
     const int32_t* map;  // mapped only: this sequence's row of the index map
     int n_slots;
     int* status;
+    // mapped, with the chunk's own K/V passed in (not yet in the cache):
+    // logical key n_first + i is token i of the chunk, at nbase + i * stride
+    const char* nbase;
+    int n_first;
 
     // Base of the 64-key tile `tile`, and the offset of its row `row`.
     template <bool MAPPED>
@@ -128,14 +132,29 @@ struct Rows {
         }
         return static_cast<uint32_t>(slot) * stride;
     }
+    // Start of row `row` of tile `tile`.
+    template <bool MAPPED>
+    __device__ __forceinline__ const char* row_addr(int tile, int row) const {
+        if constexpr (!MAPPED) {
+            return tile_base<false>(tile) + static_cast<uint32_t>(row) * stride;
+        } else {
+            const int j = tile * BN + row;
+            if (nbase && j >= n_first) return nbase + static_cast<size_t>(j - n_first) * stride;
+            return base + row_off<true>(tile, row);
+        }
+    }
 };
+// Rows of K (or V) of one (batch, kv head); `fresh` is the chunk's own K (or
+// V) when the launch also writes it to the cache (mapped only), else null.
 template <bool MAPPED>
-__device__ __forceinline__ Rows kv_rows(const RunArgs& a, const Ctx& c, const void* t, int D, int el) {
+__device__ __forceinline__ Rows kv_rows(const RunArgs& a, const Ctx& c, const void* t, const void* fresh, int D,
+                                        int el) {
     const uint32_t stride = static_cast<uint32_t>(a.n_kv_heads * D * el);
     if (MAPPED)
         return {static_cast<const char*>(t) + static_cast<size_t>(c.hkv) * D * el, stride,
-                a.kv_map + static_cast<size_t>(c.b) * a.map_stride, a.n_slots, a.status};
-    return {static_cast<const char*>(t) + kv_index(a, c, 0, D) * el, stride, nullptr, 0, nullptr};
+                a.kv_map + static_cast<size_t>(c.b) * a.map_stride, a.n_slots, a.status,
+                fresh ? static_cast<const char*>(fresh) + kv_index(a, c, 0, D) * el : nullptr, c.kshift};
+    return {static_cast<const char*>(t) + kv_index(a, c, 0, D) * el, stride, nullptr, 0, nullptr, nullptr, 0};
 }
 __device__ __forceinline__ Rows q_rows(const RunArgs& a, const Ctx& c, const void* t, int D, int el) {
     return {static_cast<const char*>(t) + q_index(a, c, 0, D) * el, static_cast<uint32_t>(a.n_heads * D * el),
@@ -150,6 +169,34 @@ __device__ __forceinline__ float* split_o(const RunArgs& a, size_t row, int spli
 __device__ __forceinline__ float2* split_ml(const RunArgs& a, size_t row, int split, int D) {
     const size_t rows = static_cast<size_t>(a.batch) * a.seq_len * a.n_heads;
     return reinterpret_cast<float2*>(a.ws + rows * a.n_split * D) + row * a.n_split + split;
+}
+
+// The chunk's own K/V rows of one query block written to their cache slots
+// (the launch reads them from the chunk's tensors, so no key of this launch
+// reads a slot written here while the map is one-to-one over the keys):
+// by the workgroups of the first split and of the first query head of each
+// kv head, each writing the tokens of its own query rows.  A slot outside
+// [0, n_slots) is skipped and sets the status word.
+template <int D, int BM, int NT>
+__device__ void store_chunk_rows(const RunArgs& a, const Ctx& c) {
+    if (c.split != 0 || c.hq % (a.n_heads / a.n_kv_heads) != 0) return;
+    constexpr int kCh = D * 2 / 16;  // 16-byte pieces of a 2-byte-element row
+    const int rows = min(BM, c.S - c.q0);
+    const int32_t* map = a.kv_map + static_cast<size_t>(c.b) * a.map_stride + c.off;
+    for (int idx = threadIdx.x; idx < rows * kCh; idx += NT) {
+        const int i = c.q0 + idx / kCh, ch = idx % kCh;
+        const int slot = map[i];
+        if (static_cast<unsigned>(slot) >= static_cast<unsigned>(a.n_slots)) {
+            if (ch == 0) atomicOr(a.status, 1);
+            continue;
+        }
+        const size_t src = kv_index(a, c, i, D) * 2 + 16 * ch;
+        const size_t dst = (static_cast<size_t>(slot) * a.n_kv_heads + c.hkv) * D * 2 + 16 * ch;
+        *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k)) + dst) =
+            *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src);
+        *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v)) + dst) =
+            *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src);
+    }
 }
 
 // Split-K variant of zero_rows: empty partials (O = 0, max = -inf, sum = 0).
@@ -200,7 +247,6 @@ struct VStage {
     // branch separates a load from its use; only the commit is guarded.
     template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load(const Rows& p, int S, int tile, Regs& r) {
-        const char* vb = p.tile_base<MAPPED>(tile);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int idx = min(static_cast<int>(threadIdx.x % NT) + NT * i, kItems - 1);
@@ -209,7 +255,7 @@ struct VStage {
             for (int rr = 0; rr < 4; ++rr) {
                 int row = 4 * kq + rr;
                 if (CLAMP) row = min(row, S - 1 - tile * BN);
-                r.raw[i][rr] = ld16(vb, p.row_off<MAPPED>(tile, row) + 16 * dc);
+                r.raw[i][rr] = ld16(p.row_addr<MAPPED>(tile, row), 16 * dc);
             }
         }
     }
@@ -290,7 +336,7 @@ struct Bf16QK {
 
     template <bool MAPPED>
     __device__ static __forceinline__ KPtr kptr(const RunArgs& a, const Ctx& c) {
-        return {kv_rows<MAPPED>(a, c, a.k, D, 2),
+        return {kv_rows<MAPPED>(a, c, a.k, a.k_new, D, 2),
                 reinterpret_cast<const char*>(a.rope_f32 + static_cast<size_t>(c.koff) * D), c.NK};
     }
 
@@ -319,7 +365,6 @@ struct Bf16QK {
     // CLAMP: the tile may reach past the last key (rows are clamped to it).
     template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
-        const char* kb = p.k.template tile_base<MAPPED>(tile);
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -327,7 +372,7 @@ struct Bf16QK {
             int row = idx / (D / 8);
             const int ch = idx % (D / 8);
             if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-            r.raw[i] = ld16(kb, p.k.template row_off<MAPPED>(tile, row) + 16 * ch);
+            r.raw[i] = ld16(p.k.template row_addr<MAPPED>(tile, row), 16 * ch);
             r.cs[i][0] = ld16(tb, (row * D + 8 * ch) * 4);
             r.cs[i][1] = ld16(tb, (row * D + 8 * ch) * 4 + 16);
         }
@@ -445,7 +490,7 @@ struct I16QK {
 
     template <bool MAPPED>
     __device__ static __forceinline__ KPtr kptr(const RunArgs& a, const Ctx& c) {
-        return {kv_rows<MAPPED>(a, c, a.k, D, 2),
+        return {kv_rows<MAPPED>(a, c, a.k, a.k_new, D, 2),
                 reinterpret_cast<const char*>(a.rope_q14 + static_cast<size_t>(c.koff) * D), c.NK};
     }
 
@@ -479,7 +524,6 @@ struct I16QK {
 
     template <bool CLAMP, bool MAPPED>
     __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
-        const char* kb = p.k.template tile_base<MAPPED>(tile);
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -487,7 +531,7 @@ struct I16QK {
             int row = idx / (D / 8);
             const int ch = idx % (D / 8);
             if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-            r.raw[i] = ld16(kb, p.k.template row_off<MAPPED>(tile, row) + 16 * ch);
+            r.raw[i] = ld16(p.k.template row_addr<MAPPED>(tile, row), 16 * ch);
             r.cs[i] = ld16(tb, (row * D + 8 * ch) * 2);
         }
     }
@@ -649,13 +693,12 @@ struct I16QuantQK : I16QK<D, NT> {
     __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
         const int tid = threadIdx.x % NT;
         const int sub = tid & 15;
-        const char* kb = p.k.template tile_base<MAPPED>(tile);
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
 #pragma unroll
         for (int i = 0; i < kPasses; ++i) {
             int row = (tid >> 4) + (NT / 16) * i;
             if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-            const uint32_t* src = reinterpret_cast<const uint32_t*>(kb + p.k.template row_off<MAPPED>(tile, row) + 2 * E * sub);
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(p.k.template row_addr<MAPPED>(tile, row) + 2 * E * sub);
             const uint32_t* t = reinterpret_cast<const uint32_t*>(tb + (row * D + E * sub) * 2);
 #pragma unroll
             for (int e = 0; e < E / 2; ++e) {
@@ -755,12 +798,11 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
         int row = tid >> 3;
         const int e0 = (tid & 7) * (D / 8);
         if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-        const char* kb = p.k.template tile_base<MAPPED>(tile);
-        const uint32_t ro = p.k.template row_off<MAPPED>(tile, row);
+        const char* kr = p.k.template row_addr<MAPPED>(tile, row);
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
 #pragma unroll
         for (int i = 0; i < kGran; ++i) {
-            r.raw[i] = *reinterpret_cast<const uint2*>(kb + ro + 2 * (e0 + 4 * i));
+            r.raw[i] = *reinterpret_cast<const uint2*>(kr + 2 * (e0 + 4 * i));
             r.cs[i] = ld16(tb, (row * D + e0 + 4 * i) * 4);
         }
     }
@@ -798,13 +840,13 @@ struct VStage8 : VStage<D, NT> {
     __device__ static __forceinline__ void load(const Rows& p, int S, int tile, Regs& r) {
         const int tid = threadIdx.x % NT;
         const int kp = tid & 31, dg = tid >> 5;
-        const char* vb = p.tile_base<MAPPED>(tile);
+
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             int row = 2 * kp + kk;
             if (CLAMP) row = min(row, S - 1 - tile * BN);
             const uint32_t* src =
-                reinterpret_cast<const uint32_t*>(vb + p.row_off<MAPPED>(tile, row) + 2 * kDims * dg);
+                reinterpret_cast<const uint32_t*>(p.row_addr<MAPPED>(tile, row) + 2 * kDims * dg);
 #pragma unroll
             for (int i = 0; i < kWords; ++i) r.w[kk][i] = src[i];
         }
@@ -1164,7 +1206,7 @@ struct FusedAttn {
             }
         }
         kp = P::template kptr<MAPPED>(a, c);
-        vp = kv_rows<MAPPED>(a, c, a.v, D, 2);
+        vp = kv_rows<MAPPED>(a, c, a.v, a.v_new, D, 2);
 
         // Prologue: K'(t_lo), K'(t_lo+1) and V^T(t_lo) in LDS; K(t_lo+2) and
         // V(t_lo+1) in registers for the first vector phase.  An empty split
@@ -1300,7 +1342,7 @@ struct FusedAttn {
             }
         }
         kp = P::template kptr<MAPPED>(a, c);
-        vp = kv_rows<MAPPED>(a, c, a.v, D, 2);
+        vp = kv_rows<MAPPED>(a, c, a.v, a.v_new, D, 2);
 
         float pwl_max = kNegInf;
         if (PWL) {
@@ -1429,6 +1471,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, floa
         }
         zero_block();
     } else {
+        if (MAPPED && a.k_new) store_chunk_rows<D, K::BMP, K::NT>(a, k.c);
         k.c.hq += hw;
         if (PP)
             k.run_pp(a, logit_scale);
@@ -1442,6 +1485,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_fwd_kernel(RunArgs a, floa
         zero_block();
         return;
     }
+    if (MAPPED && a.k_new) store_chunk_rows<D, K::BMP, K::NT>(a, k.c);
     k.c.hq += hw;
     __syncthreads();  // every wave is done with the first block's LDS tiles
     if (PP)
@@ -1469,8 +1513,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(RunArgs a, float
     const int kq0 = c.kshift + qw0;
     const int n_tiles = (c.kshift + min(c.q0 + BM, c.S) + BN - 1) / BN;
     const float* qg = static_cast<const float*>(a.q);
-    const Rows kr_ = kv_rows<MAPPED>(a, c, a.k, D, 4);
-    const Rows vr_ = kv_rows<MAPPED>(a, c, a.v, D, 4);
+    const Rows kr_ = kv_rows<MAPPED>(a, c, a.k, nullptr, D, 4);
+    const Rows vr_ = kv_rows<MAPPED>(a, c, a.v, nullptr, D, 4);
 
     // Q' of query qw0+lq: lane half lh keeps component lh of every pair (d = 2ks + lh).
     float qv[D / 2];

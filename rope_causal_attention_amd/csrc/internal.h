@@ -43,6 +43,11 @@ struct RunArgs {
     // Score-export launches of the int16 paths only: [batch][n_heads][S][S] int32
     // scores of every key at or before its query (no O is written).
     int32_t* dbg_scores;
+    // Cached prefill with the chunk's own K/V (mapped, 16-bit types): the
+    // chunk's keys are read from these [batch][seq_len][n_kv_heads][D]
+    // tensors, and the launch writes them to their cache slots in k / v.
+    const void* k_new;
+    const void* v_new;
 };
 
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t stream);

@@ -445,3 +445,83 @@ def test_split_k_range_error_gives_zeros():
         assert torch.all(torch.isfinite(o[0])) and not torch.all(o[0] == 7.0)
     finally:
         attn.close()
+
+
+# ------------------------------------------------------------ update fused into the attention launch
+
+FUSED_CASES = [
+    # name, B, Hq, Hkv, D, dtype (bf16q: bf16 quantised in-kernel), chunks, layout, n_split
+    ("fu_bf16_d96_8wave", 1, 32, 32, 96, "bf16", [1024, 1024, 512], "ring", 0),
+    ("fu_bf16_d128_gqa_split", 2, 16, 4, 128, "bf16", [300, 700, 64], "paged", 4),
+    ("fu_bf16_d64_4wave", 2, 4, 2, 64, "bf16", [100, 333, 1, 250], "paged", 1),
+    ("fu_i16_d128", 1, 8, 2, 128, "i16", [200, 456], "ring", 1),
+    ("fu_i16_d128_split", 1, 8, 2, 128, "i16", [512, 300], "paged", 3),
+    ("fu_q16_d96", 1, 4, 4, 96, "bf16q", [130, 290], "ring", 0),
+    ("fu_f32_d64", 1, 2, 2, 64, "f32", [70, 90], "paged", 1),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_run_cached_update_equals_update_then_run(case):
+    """prefill_attn_run_cached_update on each chunk against kv_cache_update then
+    run_cached(_splitk) on a copy of the same cache: every output and the final
+    caches bit for bit."""
+    name, B, Hq, Hkv, D, dt, chunks, layout, n_split = case
+    T = sum(chunks)
+    announce(name, chunks, "split", n_split)
+    w = synth.Workload(name, B, Hq, Hkv, T, D, dt, 1e4, _seed(name))
+    q, k, v = synth.make_inputs(w)
+    n_slots = B * ((T + 63) // 64) * 64 + 64
+    kv_map = _maps(layout, B, T, n_slots, _seed(name), block=64)
+    quant = dt == "bf16q"
+    scale = _score_scale(dt, D)
+    attn = pa.PrefillAttention(Hq, Hkv, D, T, 1e4)
+    try:
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        mapd = torch.from_numpy(kv_map).cuda()
+        caches = [(_garbage((n_slots, Hkv, D), "i16" if dt == "i16" else "bf16" if dt != "f32" else "f32", 7),
+                   _garbage((n_slots, Hkv, D), "f32" if dt == "f32" else "bf16", 8)) for _ in range(2)]
+        (kc1, vc1), (kc2, vc2) = [(a.cuda(), b.cuda()) for a, b in caches]
+        ws_bytes = pa.prefill_attn_run_cached_workspace_size(attn.handle, B, max(chunks), 16)
+        ws1 = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        ws2 = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        pos = 0
+        for n in chunks:
+            off = torch.full((B,), pos, dtype=torch.int32, device="cuda")
+            qc, kn, vn = (x[:, pos:pos + n].contiguous() for x in (qd, kd, vd))
+            attn.kv_cache_update(kn, vn, kc1, vc1, mapd, off)
+            o1 = attn.run_cached(qc, kc1, vc1, mapd, pos_offsets=off, score_scale=scale, quantize=quant,
+                                 n_split=n_split, workspace=ws1 if n_split != 1 else None)
+            o2 = attn.run_cached_update(qc, kn, vn, kc2, vc2, mapd, pos_offsets=off, score_scale=scale,
+                                        quantize=quant, n_split=n_split, workspace=ws2 if n_split != 1 else None)
+            torch.cuda.synchronize()
+            assert attn.status() == pa.PA_OK
+            assert torch.equal(o1, o2), f"chunk at {pos}: max diff {float((o1 - o2).abs().max()):.3e}"
+            pos += n
+        assert torch.equal(kc1, kc2) and torch.equal(vc1, vc2)
+    finally:
+        attn.close()
+
+
+def test_run_cached_update_bad_slot_is_skipped_and_reported():
+    """A map entry outside the cache for one of the chunk's own tokens: that row is
+    not written (the rest are), and the status word reads PA_ERANGE."""
+    B, Hq, Hkv, D, S = 1, 2, 2, 64, 100
+    w = synth.Workload("fu_bad_slot", B, Hq, Hkv, S, D, "bf16", 1e4, 91)
+    q, k, v = synth.make_inputs(w)
+    n_slots = 128
+    kv_map = np.arange(S, dtype=np.int32)[None, :].copy()
+    kv_map[0, 37] = n_slots + 5
+    attn = pa.PrefillAttention(Hq, Hkv, D, S, 1e4)
+    try:
+        kc = torch.zeros((n_slots, Hkv, D), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        attn.run_cached_update(q.cuda(), k.cuda(), v.cuda(), kc, vc, torch.from_numpy(kv_map).cuda())
+        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_ERANGE
+        kc, vc = kc.cpu(), vc.cpu()
+        rows = [i for i in range(S) if i != 37]
+        assert torch.equal(kc[rows], k[0, rows]) and torch.equal(vc[rows], v[0, rows])
+        assert torch.all(kc[S:] == 0)
+    finally:
+        attn.close()
