@@ -299,6 +299,7 @@ template <int D, int NT>
 struct Bf16QK {
     static constexpr int kStride = D + 8;  // f16 per K' row (16-byte pad against bank conflicts)
     static constexpr bool kSerialBlocks = false;  // the two key blocks' MFMAs may interleave
+    static constexpr bool kIntScores = false;
     static constexpr int kBytes = BN * kStride * 2;
     static constexpr int kChunks = BN * D / 8;  // 16-byte chunks per K tile
     static constexpr int kPer = (kChunks + NT - 1) / NT;
@@ -403,14 +404,16 @@ struct Bf16QK {
     }
 
     // Logits (log2 units) S^T for key block kb (32 keys) of the tile x this
-    // wave's 32 queries.  All K' fragments of the block are read from LDS
-    // before the MFMA chain is issued.
-    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh) {
+    // wave's 32 queries, plus `shift` (the MFMA's C operand: every lane's 16
+    // entries hold minus the shift of its query).  All K' fragments of the
+    // block are read from LDS before the MFMA chain is issued.
+    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh,
+                                              const f32x16& shift) {
         const _Float16* row = reinterpret_cast<const _Float16*>(lds) + (32 * kb + lq) * kStride + 8 * lh;
         f16x8 a[D / 16];
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) a[ks] = *reinterpret_cast<const f16x8*>(row + 16 * ks);
-        f32x16 acc = {};
+        f32x16 acc = shift;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], q.f[ks], acc, 0, 0, 0);
 #pragma unroll
@@ -427,6 +430,7 @@ struct I16QK {
     // time (three int32 accumulators each), which keeps the eight-wave kernels
     // within their register budget.
     static constexpr bool kSerialBlocks = true;
+    static constexpr bool kIntScores = true;
     static constexpr int kPlane = BN * kRow;
     static constexpr int kBytes = 3 * kPlane;  // planes: high digit, low digit, high + low
     static constexpr int kChunks = BN * D / 8;
@@ -572,15 +576,18 @@ struct I16QK {
         }
     }
 
-    // Logits (log2 units) of key block kb from its int32 scores: float(score) * scale.
-    __device__ static __forceinline__ void logits(const char*, int, const Q& q, const int* si, float* s, int) {
+    // Logits (log2 units) of key block kb from its int32 scores: float(score) * scale
+    // plus the shift (minus the lane's shift in every entry of `shift`).
+    __device__ static __forceinline__ void logits(const char*, int, const Q& q, const int* si, float* s, int,
+                                                  const f32x16& shift) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] = static_cast<float>(si[v]) * q.scale;
+        for (int v = 0; v < 16; ++v) s[v] = fmaf(static_cast<float>(si[v]), q.scale, shift[0]);
     }
-    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh) {
+    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh,
+                                              const f32x16& shift) {
         int si[16];
         qk_i32(lds, kb, q, si, lq, lh);
-        logits(lds, kb, q, si, s, lh);
+        logits(lds, kb, q, si, s, lh, shift);
     }
 };
 
@@ -752,21 +759,22 @@ struct I16QuantQK : I16QK<D, NT> {
     }
 
     // Logits (log2 units) from the int32 scores: float(score) * scale_q * m_k / 2047 of each key.
-    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh) {
+    __device__ static __forceinline__ void qk(const char* lds, int kb, const Q& q, float* s, int lq, int lh,
+                                              const f32x16& shift) {
         int si[16];
         Base::qk_i32(lds, kb, q, si, lq, lh);
-        logits(lds, kb, q, si, s, lh);
+        logits(lds, kb, q, si, s, lh, shift);
     }
     __device__ static __forceinline__ void logits(const char* lds, int kb, const Q& q, const int* si, float* s,
-                                                  int lh) {
+                                                  int lh, const f32x16& shift) {
         const float* inv = reinterpret_cast<const float*>(lds + kInv) + 32 * kb + 4 * lh;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const float4 f = *reinterpret_cast<const float4*>(inv + 8 * g);
-            s[4 * g + 0] = static_cast<float>(si[4 * g + 0]) * q.scale * f.x;
-            s[4 * g + 1] = static_cast<float>(si[4 * g + 1]) * q.scale * f.y;
-            s[4 * g + 2] = static_cast<float>(si[4 * g + 2]) * q.scale * f.z;
-            s[4 * g + 3] = static_cast<float>(si[4 * g + 3]) * q.scale * f.w;
+            s[4 * g + 0] = fmaf(static_cast<float>(si[4 * g + 0]) * q.scale, f.x, shift[0]);
+            s[4 * g + 1] = fmaf(static_cast<float>(si[4 * g + 1]) * q.scale, f.y, shift[0]);
+            s[4 * g + 2] = fmaf(static_cast<float>(si[4 * g + 2]) * q.scale, f.z, shift[0]);
+            s[4 * g + 3] = fmaf(static_cast<float>(si[4 * g + 3]) * q.scale, f.w, shift[0]);
         }
     }
 };
@@ -929,6 +937,32 @@ struct FusedAttn {
     typename P::Guard guard;  // range of this thread's converted Q' / K' values
     f32x16 o[D / 32];
     float m_run, l_a, l_b;
+    // kShift: the scores arrive shifted by b_run, subtracted by the Q.K^T
+    // products themselves (the C operand of the matrix-core path, the scaling
+    // FMA of the integer ones), so the softmax exponentiates them as they
+    // are.  b_run is 0 until the lane's first maximum is known, then m_run,
+    // which moves only when a tile's maximum passes it by more than the
+    // slack.  The shift rounds differently from a later subtraction, so it is
+    // chosen per head_dim and score type, never per schedule: every launch
+    // shape of one input type then gives the same bits (chunked, cached,
+    // packed and plain launches agree).  It holds 16 more registers, which
+    // every fp16 schedule at head_dim 128 has to spare; at 64 and 96 one of
+    // them would spill (the paired eight-wave 96, the two-workgroup four-wave
+    // 64), and so would the eight-wave integer ones.
+    static constexpr bool kShift = D == 128 && !P::kIntScores;
+    float b_run;
+    f32x16 nbias;  // -b_run in every entry
+    __device__ __forceinline__ void set_shift(float b) {
+        b_run = kShift ? b : 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) nbias[v] = -b_run;
+    }
+    __device__ __forceinline__ f32x16 score_shift() const {
+        if constexpr (kShift) return nbias;
+        return f32x16{};
+    }
+    // exp2 argument of a (shifted) score
+    __device__ __forceinline__ float exp_arg(float x) const { return kShift ? x : x - m_run; }
 
     __device__ __forceinline__ int slot(int t) const { return PP ? (t - t_lo) % 3 : PAIR ? ((t - t_lo) & 3) : (t & 1); }
     __device__ __forceinline__ char* kbuf(int t) const { return lds + slot(t) * P::kBytes; }
@@ -952,9 +986,9 @@ struct FusedAttn {
             if (na >= 1) qk_store(t, 0, s);
             if (na == 2) qk_store(t, 1, s + 16);
         } else {
-            if (na >= 1) P::qk(kbuf(t), 0, q, s, lq, lh);
+            if (na >= 1) P::qk(kbuf(t), 0, q, s, lq, lh, score_shift());
             if (P::kSerialBlocks) __builtin_amdgcn_sched_barrier(0);
-            if (na == 2) P::qk(kbuf(t), 1, q, s + 16, lq, lh);
+            if (na == 2) P::qk(kbuf(t), 1, q, s + 16, lq, lh, score_shift());
         }
     }
     // DBG: the int32 scores of key block kb, stored for keys at or before the
@@ -971,7 +1005,7 @@ struct FusedAttn {
                 if (key <= qi) row[key] = si[v];
             }
         }
-        P::logits(kbuf(t), kb, q, si, s, lh);
+        P::logits(kbuf(t), kb, q, si, s, lh, score_shift());
     }
     int32_t* a_dbg = nullptr;  // DBG: the score matrix, and the query head count of its layout
     int n_heads_dbg = 0;
@@ -1001,16 +1035,28 @@ struct FusedAttn {
                 for (int v = 0; v < 16; ++v) m4[PP ? (v & 3) : 0] = fmaxf(m4[PP ? (v & 3) : 0], s[16 * kb + v]);
             }
         if (PP) exp_tile(na, s, pk);
+        // the tile's maximum, in the scores' shifted frame
         const float mx = halves_max(PP ? fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) : m4[0]);
-        const bool moved = __builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0;
+        const bool moved = __builtin_amdgcn_ballot_w64(mx + b_run > m_run + kRescaleSlack) != 0;
         if (moved) {
-            const float m_new = fmaxf(m_run, mx);
+            const float m_new = fmaxf(m_run, mx + b_run);
             const float alpha = fast_exp2(m_run - m_new);
             m_run = m_new;
             l_a *= alpha;
             l_b *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+            // re-shift this tile's scores and the next tiles' products to the new max
+            if (kShift && m_new != kNegInf) {
+                const float d = m_new - b_run;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    if (kb < na) {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) s[16 * kb + v] -= d;
+                    }
+                set_shift(m_new);
+            }
         }
         if (PP && moved) exp_tile(na, s, pk);
         const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
@@ -1020,8 +1066,8 @@ struct FusedAttn {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     if (!PP)
-                        pk[8 * kb + j] = pack_h2(fast_exp2(s[16 * kb + 2 * j] - m_run),
-                                                 fast_exp2(s[16 * kb + 2 * j + 1] - m_run));
+                        pk[8 * kb + j] = pack_h2(fast_exp2(exp_arg(s[16 * kb + 2 * j])),
+                                                 fast_exp2(exp_arg(s[16 * kb + 2 * j + 1])));
                     const f16x2 p = __builtin_bit_cast(f16x2, pk[8 * kb + j]);
                     if (j & 1)
                         l_b = __builtin_amdgcn_fdot2(p, ones, l_b, false);
@@ -1038,8 +1084,8 @@ struct FusedAttn {
             if (kb < na) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    pk[8 * kb + j] = pack_h2(fast_exp2(s[16 * kb + 2 * j] - m_run),
-                                             fast_exp2(s[16 * kb + 2 * j + 1] - m_run));
+                    pk[8 * kb + j] = pack_h2(fast_exp2(exp_arg(s[16 * kb + 2 * j])),
+                                             fast_exp2(exp_arg(s[16 * kb + 2 * j + 1])));
             }
     }
 
@@ -1086,7 +1132,7 @@ struct FusedAttn {
                     for (int e = 0; e < 2; ++e) {
                         const int v = 2 * j + e;
                         const bool vis = FULL || k0 + acc_row(v, lh) <= kq0 + lq;
-                        w[e] = vis ? pwl_exp(s[16 * kb + v] - m_run) : 0.0f;
+                        w[e] = vis ? pwl_exp(s[16 * kb + v] + b_run - m_run) : 0.0f;
                     }
                     const uint32_t p = pack_h2(w[0], w[1]);
                     pk[8 * kb + j] = p;
@@ -1234,6 +1280,7 @@ struct FusedAttn {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
         m_run = kNegInf;
+        set_shift(0.f);
         l_a = 0.f;
         l_b = 0.f;
         __syncthreads();
@@ -1355,8 +1402,8 @@ struct FusedAttn {
                 __syncthreads();
                 const int na = nact(t);
                 float s1[32];
-                if (na >= 1) P::qk(kbuf(0), 0, q, s1, lq, lh);
-                if (na == 2) P::qk(kbuf(0), 1, q, s1 + 16, lq, lh);
+                if (na >= 1) P::qk(kbuf(0), 0, q, s1, lq, lh, f32x16{});
+                if (na == 2) P::qk(kbuf(0), 1, q, s1 + 16, lq, lh, f32x16{});
                 if (na > 0) pwl_max = fmaxf(pwl_max, tile_max(t, na, s1));
             }
             pwl_max = halves_max(pwl_max);
@@ -1389,6 +1436,7 @@ struct FusedAttn {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
         m_run = PWL ? pwl_max : kNegInf;
+        set_shift(PWL && pwl_max != kNegInf ? pwl_max : 0.f);
         l_a = 0.f;
         l_b = 0.f;
         __syncthreads();
