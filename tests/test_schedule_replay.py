@@ -272,10 +272,10 @@ def test_plain_and_cached_blocks(sched):
     assert set(range(1, 81)) <= counts, sorted(set(range(1, 81)) - counts)
 
 
-@pytest.mark.parametrize("sched", ["plain", "pp"])
+@pytest.mark.parametrize("sched", ["plain", "pp", "pair"])
 def test_split_ranges(sched):
-    """Split-K runs the plain schedule (four-wave) and PP (head_dim 128)."""
-    bmp = 256 if sched == "pp" else 128
+    """Split-K runs the plain schedule (four-wave), PP (head_dim 128) and PAIR (eight-wave, 64 and 96)."""
+    bmp = 128 if sched == "plain" else 256
     seen = set()
     for n_all in range(0, 81):
         for n_split in range(1, 9):
