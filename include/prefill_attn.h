@@ -98,8 +98,8 @@ enum prefill_attn_status {
  *   max_seq     largest position + 1 any run may use (table rows), 1 .. 1048576
  *   rope_theta  RoPE base, > 1
  * Builds the RoPE cos/sin tables on the host in fp64 (each value rounded once, to
- * fp32 pairs for the fp32 path and decode, to fp16 pairs for the bf16 paths and
- * to Q1.14 int16 pairs for the int16 paths), copies them to the device and
+ * fp32 pairs for the fp32 and bf16 paths and decode, and to Q1.14 int16 pairs
+ * for the int16 paths), copies them to the device and
  * allocates the status word.  All allocation happens here; prefill_attn_run
  * allocates nothing.
  * On success *out receives the handle; on failure *out is set to NULL.
@@ -330,16 +330,12 @@ const char* prefill_attn_strerror(int code);
  * evaluated in fp64:
  *   _f32: out[(p*head_dim/2 + k)*2 + 0] = (float)cos(a), [... + 1] = (float)sin(a)
  *         (round to nearest even), out has max_seq*head_dim floats;
- *   _f16: the same layout with each value rounded once from fp64 to IEEE binary16
- *         (nearest even), out has max_seq*head_dim uint16 (the bit patterns); the
- *         bf16 prefill kernels rotate Q and K with this table;
  *   _q14: out[(p*head_dim/2 + k)*2 + 0] = round(cos(a) * 2^14), [... + 1] = round(sin(a) * 2^14)
  *         (nearest, ties away from zero), out has max_seq*head_dim int16.
  * head_dim must be even and positive, max_seq positive; out is caller-owned host memory.
  */
 int prefill_attn_rope_table_f32(int max_seq, int head_dim, double rope_theta, float* out);
 int prefill_attn_rope_table_q14(int max_seq, int head_dim, double rope_theta, int16_t* out);
-int prefill_attn_rope_table_f16(int max_seq, int head_dim, double rope_theta, uint16_t* out);
 
 /*
  * Test exports for the int16 variant, run by the device code of PA_IN_I16:

@@ -24,7 +24,6 @@ __all__ = [
     "PrefillAttnError", "load_library", "library_path",
     "prefill_attn_init", "prefill_attn_run", "prefill_attn_status", "prefill_attn_destroy",
     "prefill_attn_strerror", "prefill_attn_rope_table_f32", "prefill_attn_rope_table_q14",
-    "prefill_attn_rope_table_f16",
     "prefill_attn_debug_rope_i16", "prefill_attn_debug_scores_i32", "prefill_attn_debug_scores_q16",
     "prefill_attn_kv_cache_update", "prefill_attn_run_cached", "prefill_attn_ring_map", "prefill_attn_paged_map",
     "prefill_attn_decode", "prefill_attn_decode_workspace_size",
@@ -50,7 +49,6 @@ _SIGNATURES = {
     "prefill_attn_strerror": (ctypes.c_char_p, [_I]),
     "prefill_attn_rope_table_f32": (_I, [_I, _I, ctypes.c_double, _P]),
     "prefill_attn_rope_table_q14": (_I, [_I, _I, ctypes.c_double, _P]),
-    "prefill_attn_rope_table_f16": (_I, [_I, _I, ctypes.c_double, _P]),
     "prefill_attn_debug_rope_i16": (_I, [_P, _I, _I, _P, _I, _P, _P, _P]),
     "prefill_attn_debug_scores_i32": (_I, [_P, _I, _I, _P, _P, _P, _P, _P]),
     "prefill_attn_debug_scores_q16": (_I, [_P, _I, _I, _P, _P, _P, _P, _P]),
@@ -191,14 +189,6 @@ def prefill_attn_rope_table_q14(max_seq, head_dim, rope_theta):
     out = np.empty((max_seq, head_dim // 2, 2), dtype=np.int16)
     _check(load_library().prefill_attn_rope_table_q14(max_seq, head_dim, float(rope_theta),
                                                       out.ctypes.data), "prefill_attn_rope_table_q14")
-    return out
-
-
-def prefill_attn_rope_table_f16(max_seq, head_dim, rope_theta):
-    """Host table [max_seq][head_dim/2][2] float16 (cos, sin)."""
-    out = np.empty((max_seq, head_dim // 2, 2), dtype=np.float16)
-    _check(load_library().prefill_attn_rope_table_f16(max_seq, head_dim, float(rope_theta),
-                                                      out.ctypes.data), "prefill_attn_rope_table_f16")
     return out
 
 

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libprefill_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.cpp", "rope_table.cpp", "attn_kernels.hip", "prefill_bf16.hip", "decode_kernels.hip", "device_peak.hip"]
+SOURCES = ["api.cpp", "rope_table.cpp", "attn_kernels.hip", "decode_kernels.hip", "device_peak.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 # Packed fp32 VALU forms are switched off for all device code.

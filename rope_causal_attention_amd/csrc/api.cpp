@@ -27,7 +27,6 @@ struct prefill_attn {
     double rope_theta;
     float* d_rope_f32;
     int16_t* d_rope_q14;
-    uint16_t* d_rope_h2;
     int* d_status;
 };
 
@@ -42,7 +41,6 @@ void free_handle(prefill_attn* h) {
     if (!h) return;
     if (h->d_rope_f32) (void)hipFree(h->d_rope_f32);
     if (h->d_rope_q14) (void)hipFree(h->d_rope_q14);
-    if (h->d_rope_h2) (void)hipFree(h->d_rope_h2);
     if (h->d_status) (void)hipFree(h->d_status);
     delete h;
 }
@@ -58,7 +56,6 @@ int prepare(const prefill_attn* h, int batch, int seq_len, const int32_t* pos_of
     a.pos_offsets = pos_offsets;
     a.rope_f32 = h->d_rope_f32;
     a.rope_q14 = h->d_rope_q14;
-    a.rope_h2 = reinterpret_cast<const uint32_t*>(h->d_rope_h2);
     a.status = h->d_status;
     a.batch = batch;
     a.seq_len = seq_len;
@@ -88,30 +85,26 @@ extern "C" int prefill_attn_init(prefill_attn** out, int n_heads, int n_kv_heads
     const size_t n = static_cast<size_t>(max_seq) * head_dim;  // (cos, sin) pairs x D/2 per row
     std::vector<float> t32;
     std::vector<int16_t> t14;
-    std::vector<uint16_t> th;
     try {
         t32.resize(n);
         t14.resize(n);
-        th.resize(n);
     } catch (const std::bad_alloc&) {
         return PA_ENOMEM;
     }
-    if (pa::build_rope_tables(max_seq, head_dim, rope_theta, t32.data(), th.data(), t14.data()) != PA_OK)
+    if (pa::build_rope_tables(max_seq, head_dim, rope_theta, t32.data(), t14.data()) != PA_OK)
         return PA_EINVAL;
 
     prefill_attn* h = new (std::nothrow) prefill_attn{dev, n_heads, n_kv_heads, head_dim, max_seq, rope_theta,
-                                                      nullptr, nullptr, nullptr, nullptr};
+                                                      nullptr, nullptr, nullptr};
     if (!h) return PA_ENOMEM;
     if (hipMalloc(&h->d_rope_f32, n * sizeof(float)) != hipSuccess ||
         hipMalloc(&h->d_rope_q14, n * sizeof(int16_t)) != hipSuccess ||
-        hipMalloc(&h->d_rope_h2, n * sizeof(uint16_t)) != hipSuccess ||
         hipMalloc(&h->d_status, sizeof(int)) != hipSuccess) {
         free_handle(h);
         return PA_ENOMEM;
     }
     if (hipMemcpy(h->d_rope_f32, t32.data(), n * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(h->d_rope_q14, t14.data(), n * sizeof(int16_t), hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(h->d_rope_h2, th.data(), n * sizeof(uint16_t), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemset(h->d_status, 0, sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         free_handle(h);
         return PA_ELAUNCH;

@@ -16,7 +16,6 @@ struct RunArgs {
     float* out;
     const float* rope_f32;       // [max_seq][head_dim/2] (cos, sin) fp32 pairs
     const int16_t* rope_q14;     // [max_seq][head_dim/2] (C, S) Q1.14 pairs
-    const uint32_t* rope_h2;     // [max_seq][head_dim/2] (cos, sin) fp16 pairs, cos in the low half
     int* status;                 // bit 0: a position left the table or map; bit 1: a value left its range
     int batch;
     int seq_len;
@@ -51,10 +50,6 @@ struct RunArgs {
 };
 
 hipError_t launch_attn_bf16(int head_dim, const RunArgs& a, hipStream_t stream);
-// bf16 prefill with K, V and table rows DMA'd into LDS (plain, unsplit launches
-// of eight-wave workgroups at head_dim 64 and 96).
-bool prefill_lds_supported(int head_dim, const RunArgs& a);
-hipError_t launch_prefill_lds(int head_dim, const RunArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(int head_dim, const RunArgs& a, hipStream_t stream);
 hipError_t launch_attn_i16(int head_dim, const RunArgs& a, hipStream_t stream);
 // bf16 Q/K quantised in-kernel per (token, head) row to int16, then the int16 path.
@@ -121,8 +116,8 @@ hipError_t launch_debug_rope_i16(int head_dim, const RunArgs& a, int n_heads_x, 
 hipError_t launch_debug_scores_i32(int head_dim, const RunArgs& a, int32_t* dst, hipStream_t stream);
 hipError_t launch_debug_scores_q16(int head_dim, const RunArgs& a, int32_t* dst, hipStream_t stream);
 
-// Host: the fp32, fp16 and Q1.14 RoPE tables of init from one fp64 pass
+// Host: the fp32 and Q1.14 RoPE tables of init from one fp64 pass
 // (each value rounded once, as the exported single-table builders do).
-int build_rope_tables(int max_seq, int head_dim, double rope_theta, float* f32, uint16_t* f16, int16_t* q14);
+int build_rope_tables(int max_seq, int head_dim, double rope_theta, float* f32, int16_t* q14);
 
 }  // namespace pa

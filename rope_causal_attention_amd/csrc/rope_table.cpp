@@ -33,9 +33,9 @@ std::vector<double> inverse_frequencies(int head_dim, double rope_theta) {
     return inv;
 }
 
-// Fills any of the three tables (null pointers are skipped) from one fp64
-// evaluation of each angle's cos and sin.
-void fill_tables(int max_seq, int head_dim, double rope_theta, float* f32, uint16_t* f16, int16_t* q14) {
+// Fills either table (a null pointer is skipped) from one fp64 evaluation of
+// each angle's cos and sin.
+void fill_tables(int max_seq, int head_dim, double rope_theta, float* f32, int16_t* q14) {
     const int half = head_dim / 2;
     const std::vector<double> inv = inverse_frequencies(head_dim, rope_theta);
     for (int p = 0; p < max_seq; ++p) {
@@ -46,11 +46,6 @@ void fill_tables(int max_seq, int head_dim, double rope_theta, float* f32, uint1
             if (f32) {
                 f32[row + 2 * k + 0] = static_cast<float>(c);
                 f32[row + 2 * k + 1] = static_cast<float>(s);
-            }
-            if (f16) {
-                // fp64 -> fp16 in one rounding (nearest even)
-                f16[row + 2 * k + 0] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(c));
-                f16[row + 2 * k + 1] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(s));
             }
             if (q14) {
                 // |cos|, |sin| <= 1, so the rounded value lies in [-16384, 16384]: fits int16.
@@ -64,28 +59,22 @@ void fill_tables(int max_seq, int head_dim, double rope_theta, float* f32, uint1
 }  // namespace
 
 namespace pa {
-// All three tables from one pass (used by init).
-int build_rope_tables(int max_seq, int head_dim, double rope_theta, float* f32, uint16_t* f16, int16_t* q14) {
-    if (!table_args_ok(max_seq, head_dim, rope_theta, f32) || !f16 || !q14) return PA_EINVAL;
-    fill_tables(max_seq, head_dim, rope_theta, f32, f16, q14);
+// The fp32 and Q1.14 tables from one pass (used by init).
+int build_rope_tables(int max_seq, int head_dim, double rope_theta, float* f32, int16_t* q14) {
+    if (!table_args_ok(max_seq, head_dim, rope_theta, f32) || !q14) return PA_EINVAL;
+    fill_tables(max_seq, head_dim, rope_theta, f32, q14);
     return PA_OK;
 }
 }  // namespace pa
 
 extern "C" int prefill_attn_rope_table_f32(int max_seq, int head_dim, double rope_theta, float* out) {
     if (!table_args_ok(max_seq, head_dim, rope_theta, out)) return PA_EINVAL;
-    fill_tables(max_seq, head_dim, rope_theta, out, nullptr, nullptr);
-    return PA_OK;
-}
-
-extern "C" int prefill_attn_rope_table_f16(int max_seq, int head_dim, double rope_theta, uint16_t* out) {
-    if (!table_args_ok(max_seq, head_dim, rope_theta, out)) return PA_EINVAL;
-    fill_tables(max_seq, head_dim, rope_theta, nullptr, out, nullptr);
+    fill_tables(max_seq, head_dim, rope_theta, out, nullptr);
     return PA_OK;
 }
 
 extern "C" int prefill_attn_rope_table_q14(int max_seq, int head_dim, double rope_theta, int16_t* out) {
     if (!table_args_ok(max_seq, head_dim, rope_theta, out)) return PA_EINVAL;
-    fill_tables(max_seq, head_dim, rope_theta, nullptr, nullptr, out);
+    fill_tables(max_seq, head_dim, rope_theta, nullptr, out);
     return PA_OK;
 }

@@ -47,16 +47,6 @@ def test_f32_table_matches_oracle_bitwise(max_seq, D, theta):
     assert np.array_equal(t[..., 1], sin.astype(np.float32))
 
 
-@pytest.mark.parametrize("max_seq,D,theta", [(64, 64, 1e4), (4096, 96, 1e4), (512, 128, 1e6), (33, 2, 500.0)])
-def test_f16_table_matches_oracle_bitwise(max_seq, D, theta):
-    # one rounding from the fp64 angle functions to binary16 (numpy's conversion
-    # is correctly rounded, nearest even)
-    t = pa.prefill_attn_rope_table_f16(max_seq, D, theta)
-    cos, sin = oracle.rope_cos_sin(np.arange(max_seq), D, theta)
-    assert np.array_equal(t[..., 0], cos.astype(np.float16))
-    assert np.array_equal(t[..., 1], sin.astype(np.float16))
-
-
 @pytest.mark.parametrize("max_seq,D,theta", [(2048, 128, 1e4), (300, 96, 1e6), (64, 64, 1e4)])
 def test_q14_table_matches_oracle_bitwise(max_seq, D, theta):
     t = pa.prefill_attn_rope_table_q14(max_seq, D, theta)
@@ -73,8 +63,6 @@ def test_table_builder_rejects_bad_arguments():
     assert lib.prefill_attn_rope_table_f32(1, 64, -1.0, buf.ctypes.data) == pa.PA_EINVAL
     assert lib.prefill_attn_rope_table_f32(1, 64, math.nan, buf.ctypes.data) == pa.PA_EINVAL
     assert lib.prefill_attn_rope_table_q14(1, 64, 1e4, None) == pa.PA_EINVAL
-    assert lib.prefill_attn_rope_table_f16(1, 63, 1e4, buf.ctypes.data) == pa.PA_EINVAL
-    assert lib.prefill_attn_rope_table_f16(1, 64, 1e4, None) == pa.PA_EINVAL
 
 
 @pytest.mark.parametrize("args", [
