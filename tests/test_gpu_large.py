@@ -5,7 +5,9 @@
   * positions at the very end of the largest table init accepts (2^20 rows),
     for the bf16 and the int16 paths, and one past it;
   * launches of thousands of workgroups (a large batch of GQA heads packed four
-    to a workgroup, and a large MHA batch).
+    to a workgroup, and a large MHA batch);
+  * decode over a 65,536-token context, and a cached prefill chunk after a
+    60,000-token prefix (the fused cache update, split-K chosen by the library).
 
 The oracle evaluates sampled output rows one by one (oracle.attention_rows and
 its int16 twin), always including the first and last rows, rows at the tile
@@ -19,7 +21,7 @@ import torch
 import oracle
 import rope_causal_attention_amd as pa
 import synth
-from gpu_common import announce, assert_close, need_gpu, oracle_full, oracle_rows, run_gpu, sample_rows, to_dev
+from gpu_common import announce, assert_close, errors, need_gpu, oracle_full, oracle_rows, run_gpu, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -108,3 +110,58 @@ def test_many_workgroups_sampled_rows(case):
     rows = sorted(rows)
     mx, mean = assert_close(_rows_of(got, rows), oracle_rows(w, q, k, v, rows), "bf16")
     announce("margin", name, f"max {mx:.3e} mean {mean:.3e} over {len(rows)} rows")
+
+
+def test_decode_long_context():
+    """Two sequences with 65,536 and 40,001 cached tokens, 32 query / 8 KV heads,
+    head_dim 128, a bf16 paged cache of shuffled 64-slot blocks; the library
+    picks the split.  Decode computes in fp32: the fp32 bar, 1e-5."""
+    from test_gpu_decode import TOL, Decode
+    c = Decode("dec_ctx65536", 2, 32, 8, 128, "bf16", [65535, 40000], block=64)
+    announce(c.name)
+    mx, mean = errors(c.run().numpy(), c.oracle())
+    announce("margin", c.name, f"max {mx:.3e} mean {mean:.3e}")
+    assert mx <= TOL, mx
+
+
+def test_cached_prefill_after_a_long_prefix():
+    """A 1000-token chunk after 60,000 cached tokens (GQA 8/2, head_dim 96, bf16,
+    shuffled 64-slot blocks) through prefill_attn_run_cached_update with the
+    split chosen by the library: the chunk's rows land in their slots bit for
+    bit, and sampled output rows match the oracle."""
+    B, Hq, Hkv, D, block, P, S = 1, 8, 2, 96, 64, 60000, 1000
+    T = P + S
+    need = (T + block - 1) // block
+    n_slots = (need + 3) * block
+    rng = np.random.default_rng(5300)
+    kv_map = oracle.paged_index_map(rng.permutation(need + 3)[:need], block, T)[None].astype(np.int32)
+    g = torch.Generator().manual_seed(5300)
+    kc = torch.randn((n_slots, Hkv, D), generator=g).to(torch.bfloat16)
+    vc = torch.randn((n_slots, Hkv, D), generator=g).to(torch.bfloat16)
+    q = torch.randn((B, S, Hq, D), generator=g).to(torch.bfloat16)
+    kn = torch.randn((B, S, Hkv, D), generator=g).to(torch.bfloat16)
+    vn = torch.randn((B, S, Hkv, D), generator=g).to(torch.bfloat16)
+    announce("cached_prefix60000_chunk1000_d96")
+    attn = pa.PrefillAttention(Hq, Hkv, D, T, 1e4)
+    try:
+        kcd, vcd = kc.cuda(), vc.cuda()
+        ws = torch.empty(pa.prefill_attn_run_cached_workspace_size(attn.handle, B, S, 16), dtype=torch.uint8,
+                         device="cuda")
+        off = torch.tensor([P], dtype=torch.int32, device="cuda")
+        o = attn.run_cached_update(q.cuda(), kn.cuda(), vn.cuda(), kcd, vcd, torch.from_numpy(kv_map).cuda(),
+                                   pos_offsets=off, n_split=0, workspace=ws)
+        torch.cuda.synchronize()
+        assert attn.status() == pa.PA_OK
+        o, kcd, vcd = o.cpu(), kcd.cpu(), vcd.cpu()
+    finally:
+        attn.close()
+    bits = lambda t: t.view(torch.int16).numpy()  # noqa: E731
+    k_want, v_want = oracle.kv_cache_update(bits(kc), bits(vc), bits(kn), bits(vn), kv_map, prefix=[P])
+    assert np.array_equal(bits(kcd), k_want) and np.array_equal(bits(vcd), v_want)
+    rows = {(0, h, i) for h in (0, 3, 7) for i in (0, 1, 63, 64, 500, S - 1)}
+    rows |= {(0, int(rng.integers(Hq)), int(rng.integers(S))) for _ in range(12)}
+    rows = sorted(rows)
+    f = synth.to_f64
+    want = oracle.attention_cached_rows(f(q), f(kcd), f(vcd), kv_map, rows, prefix=[P])
+    mx, mean = assert_close(_rows_of(o, rows), want, "bf16")
+    announce("margin", "cached_prefix60000_chunk1000_d96", f"max {mx:.3e} mean {mean:.3e} over {len(rows)} rows")
