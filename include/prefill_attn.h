@@ -110,7 +110,7 @@ int prefill_attn_init(prefill_attn** out, int n_heads, int n_kv_heads, int head_
 /*
  * Enqueue one fused attention pass on `stream` (a hipStream_t; NULL = the null
  * stream).  Asynchronous: returns once the kernel is queued; no host sync, no
- * allocation.
+ * allocation, no memset, so the call may be captured into a HIP graph.
  *   in_dtype     a prefill_attn_dtype value
  *   batch        >= 0; seq_len in 0 .. max_seq (batch == 0 or seq_len == 0 is a no-op)
  *   q, k, v      device tensors in the layouts above, of in_dtype (V is bf16 for PA_IN_I16)
