@@ -132,18 +132,43 @@ struct Rows {
         }
         return static_cast<uint32_t>(slot) * stride;
     }
-    // Start of row `row` of tile `tile`.
+    // Start of row `row` of tile `tile`.  Mapped: `pre`, when given, holds the
+    // row's checked slot offset (as row_off forms it) read ahead of time, so
+    // the row's load does not wait for its map entry.
     template <bool MAPPED>
-    __device__ __forceinline__ const char* row_addr(int tile, int row) const {
+    __device__ __forceinline__ const char* row_addr(int tile, int row, const uint32_t* pre = nullptr) const {
         if constexpr (!MAPPED) {
             return tile_base<false>(tile) + static_cast<uint32_t>(row) * stride;
         } else {
             const int j = tile * BN + row;
             if (nbase && j >= n_first) return nbase + static_cast<size_t>(j - n_first) * stride;
-            return base + row_off<true>(tile, row);
+            return base + (pre ? *pre : row_off<true>(tile, row));
         }
     }
 };
+// Mapped launches: the map entries (unchecked slots) of the N key rows a
+// thread stages from tile `tile` (row_of(n) is its n-th row; rows past the
+// last key clamped to it as the clamped loads do; for a full tile the clamp
+// changes nothing).  Nothing here uses the values, so their loads stay in
+// flight beside the tile loads issued before them.  The entries of keys read
+// from the chunk's own tensor are read too but not used (the cache update
+// checks those).
+template <int N, class RowOf>
+__device__ __forceinline__ void read_slots(const Rows& p, int n_keys, int tile, uint32_t (&slot)[N], RowOf row_of) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) slot[n] = p.map[min(tile * BN + row_of(n), n_keys - 1)];
+}
+// The slots' byte offsets; a slot outside [0, n_slots) reads slot 0 (as
+// row_off) and sets `bad`, which the caller reports in the status word.
+template <int N>
+__device__ __forceinline__ void slot_offsets(const Rows& p, uint32_t (&slot)[N], bool& bad) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const bool ok = slot[n] < static_cast<uint32_t>(p.n_slots);
+        bad |= !ok;
+        slot[n] = (ok ? slot[n] : 0u) * p.stride;
+    }
+}
 // Rows of K (or V) of one (batch, kv head); `fresh` is the chunk's own K (or
 // V) when the launch also writes it to the cache (mapped only), else null.
 template <bool MAPPED>
@@ -245,8 +270,14 @@ struct VStage {
     __device__ static __forceinline__ bool has(int i) { return kItems % NT == 0 || static_cast<int>(threadIdx.x % NT) + NT * i < kItems; }
     // Loads are unconditional (surplus threads re-read the last item) so that no
     // branch separates a load from its use; only the commit is guarded.
+    // The key rows a thread reads: row_of(4 i + rr) for item i, key rr of its quad.
+    static constexpr int kRows = 4 * kPer;
+    __device__ static __forceinline__ int row_of(int n) {
+        return 4 * (min(static_cast<int>(threadIdx.x % NT) + NT * (n >> 2), kItems - 1) & 15) + (n & 3);
+    }
+    // pre (mapped only): the rows' slot offsets read ahead (read_slots), else null.
     template <bool CLAMP, bool MAPPED>
-    __device__ static __forceinline__ void load(const Rows& p, int S, int tile, Regs& r) {
+    __device__ static __forceinline__ void load(const Rows& p, int S, int tile, Regs& r, const uint32_t* pre = nullptr) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int idx = min(static_cast<int>(threadIdx.x % NT) + NT * i, kItems - 1);
@@ -255,7 +286,7 @@ struct VStage {
             for (int rr = 0; rr < 4; ++rr) {
                 int row = 4 * kq + rr;
                 if (CLAMP) row = min(row, S - 1 - tile * BN);
-                r.raw[i][rr] = ld16(p.row_addr<MAPPED>(tile, row), 16 * dc);
+                r.raw[i][rr] = ld16(p.row_addr<MAPPED>(tile, row, pre ? pre + 4 * i + rr : nullptr), 16 * dc);
             }
         }
     }
@@ -300,6 +331,7 @@ struct Bf16QK {
     static constexpr int kStride = D + 8;  // f16 per K' row (16-byte pad against bank conflicts)
     static constexpr bool kSerialBlocks = false;  // the two key blocks' MFMAs may interleave
     static constexpr bool kIntScores = false;
+    static constexpr bool kSlotsAhead = true;  // room for the mapped launches' slot offsets
     static constexpr int kBytes = BN * kStride * 2;
     static constexpr int kChunks = BN * D / 8;  // 16-byte chunks per K tile
     static constexpr int kPer = (kChunks + NT - 1) / NT;
@@ -363,9 +395,15 @@ struct Bf16QK {
 
     __device__ static __forceinline__ bool has(int i) { return kChunks % NT == 0 || static_cast<int>(threadIdx.x % NT) + NT * i < kChunks; }
 
+    // The key rows a thread reads: row_of(i) for chunk i.
+    static constexpr int kRows = kPer;
+    __device__ static __forceinline__ int row_of(int i) {
+        return min(static_cast<int>(threadIdx.x % NT) + NT * i, kChunks - 1) / (D / 8);
+    }
     // CLAMP: the tile may reach past the last key (rows are clamped to it).
+    // pre (mapped only): the rows' slot offsets read ahead (read_slots), else null.
     template <bool CLAMP, bool MAPPED>
-    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
+    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r, const uint32_t* pre = nullptr) {
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -373,7 +411,7 @@ struct Bf16QK {
             int row = idx / (D / 8);
             const int ch = idx % (D / 8);
             if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-            r.raw[i] = ld16(p.k.template row_addr<MAPPED>(tile, row), 16 * ch);
+            r.raw[i] = ld16(p.k.template row_addr<MAPPED>(tile, row, pre ? pre + i : nullptr), 16 * ch);
             r.cs[i][0] = ld16(tb, (row * D + 8 * ch) * 4);
             r.cs[i][1] = ld16(tb, (row * D + 8 * ch) * 4 + 16);
         }
@@ -431,6 +469,7 @@ struct I16QK {
     // within their register budget.
     static constexpr bool kSerialBlocks = true;
     static constexpr bool kIntScores = true;
+    static constexpr bool kSlotsAhead = true;
     static constexpr int kPlane = BN * kRow;
     static constexpr int kBytes = 3 * kPlane;  // planes: high digit, low digit, high + low
     static constexpr int kChunks = BN * D / 8;
@@ -526,8 +565,13 @@ struct I16QK {
 
     __device__ static __forceinline__ bool has(int i) { return kChunks % NT == 0 || static_cast<int>(threadIdx.x % NT) + NT * i < kChunks; }
 
+    // The key rows a thread reads, as Bf16QK.
+    static constexpr int kRows = kPer;
+    __device__ static __forceinline__ int row_of(int i) {
+        return min(static_cast<int>(threadIdx.x % NT) + NT * i, kChunks - 1) / (D / 8);
+    }
     template <bool CLAMP, bool MAPPED>
-    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
+    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r, const uint32_t* pre = nullptr) {
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -535,7 +579,7 @@ struct I16QK {
             int row = idx / (D / 8);
             const int ch = idx % (D / 8);
             if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-            r.raw[i] = ld16(p.k.template row_addr<MAPPED>(tile, row), 16 * ch);
+            r.raw[i] = ld16(p.k.template row_addr<MAPPED>(tile, row, pre ? pre + i : nullptr), 16 * ch);
             r.cs[i] = ld16(tb, (row * D + 8 * ch) * 2);
         }
     }
@@ -641,6 +685,9 @@ struct I16QuantQK : I16QK<D, NT> {
     using KPtr = typename Base::KPtr;
     // Codes in [-2048, 2047] rotate to at most 2897 in magnitude: always exact.
     using Guard = NoGuard;
+    // At head_dim 128 the four-wave kernel has no registers for the slot
+    // offsets of its 8 K / V rows (they spilled).
+    static constexpr bool kSlotsAhead = D < 128;
     struct KRegs {
         uint32_t raw[kPasses][E / 2];  // bf16 pairs
         uint32_t cs[kPasses][E / 2];   // Q1.14 (C, S) pairs
@@ -696,8 +743,10 @@ struct I16QuantQK : I16QK<D, NT> {
     }
 
     // K: 16 lanes per key row, lane sub holds elements [E sub, E sub + E).
+    static constexpr int kRows = kPasses;
+    __device__ static __forceinline__ int row_of(int i) { return static_cast<int>(threadIdx.x % NT) / 16 + (NT / 16) * i; }
     template <bool CLAMP, bool MAPPED>
-    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
+    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r, const uint32_t* pre = nullptr) {
         const int tid = threadIdx.x % NT;
         const int sub = tid & 15;
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 2);
@@ -705,7 +754,8 @@ struct I16QuantQK : I16QK<D, NT> {
         for (int i = 0; i < kPasses; ++i) {
             int row = (tid >> 4) + (NT / 16) * i;
             if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-            const uint32_t* src = reinterpret_cast<const uint32_t*>(p.k.template row_addr<MAPPED>(tile, row) + 2 * E * sub);
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                p.k.template row_addr<MAPPED>(tile, row, pre ? pre + i : nullptr) + 2 * E * sub);
             const uint32_t* t = reinterpret_cast<const uint32_t*>(tb + (row * D + E * sub) * 2);
 #pragma unroll
             for (int e = 0; e < E / 2; ++e) {
@@ -800,13 +850,15 @@ struct Bf16Stage8 : Bf16QK<D, NT> {
         uint2 raw[kGran];
         uint4 cs[kGran];  // fp32 (cos, sin) of the granule's 2 pairs
     };
+    static constexpr int kRows = 1;  // the key row a thread reads
+    __device__ static __forceinline__ int row_of(int) { return static_cast<int>(threadIdx.x % NT) >> 3; }
     template <bool CLAMP, bool MAPPED>
-    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r) {
+    __device__ static __forceinline__ void load_k(const KPtr& p, int tile, KRegs& r, const uint32_t* pre = nullptr) {
         const int tid = threadIdx.x % NT;
         int row = tid >> 3;
         const int e0 = (tid & 7) * (D / 8);
         if (CLAMP) row = min(row, p.S - 1 - tile * BN);
-        const char* kr = p.k.template row_addr<MAPPED>(tile, row);
+        const char* kr = p.k.template row_addr<MAPPED>(tile, row, pre);
         const char* tb = p.tab + static_cast<size_t>(tile * BN) * (D * 4);
 #pragma unroll
         for (int i = 0; i < kGran; ++i) {
@@ -844,8 +896,10 @@ struct VStage8 : VStage<D, NT> {
     struct Regs {
         uint32_t w[2][kWords];
     };
+    static constexpr int kRows = 2;  // the key rows a thread reads: keys 2 kp and 2 kp + 1
+    __device__ static __forceinline__ int row_of(int kk) { return 2 * (static_cast<int>(threadIdx.x % NT) & 31) + kk; }
     template <bool CLAMP, bool MAPPED>
-    __device__ static __forceinline__ void load(const Rows& p, int S, int tile, Regs& r) {
+    __device__ static __forceinline__ void load(const Rows& p, int S, int tile, Regs& r, const uint32_t* pre = nullptr) {
         const int tid = threadIdx.x % NT;
         const int kp = tid & 31, dg = tid >> 5;
 
@@ -853,8 +907,8 @@ struct VStage8 : VStage<D, NT> {
         for (int kk = 0; kk < 2; ++kk) {
             int row = 2 * kp + kk;
             if (CLAMP) row = min(row, S - 1 - tile * BN);
-            const uint32_t* src =
-                reinterpret_cast<const uint32_t*>(p.row_addr<MAPPED>(tile, row) + 2 * kDims * dg);
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                p.row_addr<MAPPED>(tile, row, pre ? pre + kk : nullptr) + 2 * kDims * dg);
 #pragma unroll
             for (int i = 0; i < kWords; ++i) r.w[kk][i] = src[i];
         }
@@ -933,6 +987,35 @@ struct FusedAttn {
     Rows vp;
     typename P::KRegs kr;
     typename V::Regs vr;
+    // Mapped: the slot offsets of this thread's rows of the next K and V tiles
+    // to stage, read one step before their loads so that a load does not wait
+    // for its map entry (without them every step waited for the map reads
+    // before its tile loads: the cached launches ran 20-60% slower than plain
+    // ones).  They take P::kRows + V::kRows registers; a policy without them
+    // to spare (P::kSlotsAhead false) reads each row's entry just before it.
+    static constexpr bool kAhead = MAPPED && P::kSlotsAhead;
+    uint32_t km[kAhead ? P::kRows : 1], vm[kAhead ? V::kRows : 1];
+    bool slot_bad;  // a slot read ahead was outside the cache (reported by finish)
+    __device__ __forceinline__ void read_k_slots(int tile) {
+        if constexpr (kAhead) read_slots(kp.k, c.NK, tile, km, [](int n) { return P::row_of(n); });
+    }
+    __device__ __forceinline__ void read_v_slots(int tile) {
+        if constexpr (kAhead) read_slots(vp, c.NK, tile, vm, [](int n) { return V::row_of(n); });
+    }
+    // Loads of the next K / V tile in the pipeline (tile = the previous one + 1),
+    // then the map entries of the tile after it.
+    template <bool CLAMP>
+    __device__ __forceinline__ void next_k(int tile) {
+        if constexpr (kAhead) slot_offsets(kp.k, km, slot_bad);
+        P::template load_k<CLAMP, MAPPED>(kp, tile, kr, kAhead ? km : nullptr);
+        read_k_slots(tile + 1);
+    }
+    template <bool CLAMP>
+    __device__ __forceinline__ void next_v(int tile) {
+        if constexpr (kAhead) slot_offsets(vp, vm, slot_bad);
+        V::template load<CLAMP, MAPPED>(vp, c.NK, tile, vr, kAhead ? vm : nullptr);
+        read_v_slots(tile + 1);
+    }
     typename P::Q q;
     typename P::Guard guard;  // range of this thread's converted Q' / K' values
     f32x16 o[D / 32];
@@ -1163,8 +1246,8 @@ struct FusedAttn {
     __device__ __forceinline__ void step(int t, float* s, float* sn, bool bar = true) {
         const bool ld_k = STEADY || t + KA < n_tiles;
         const bool ld_v = STEADY || t + VA < n_tiles;
-        if (ld_k) P::template load_k<!STEADY, MAPPED>(kp, t + KA, kr);
-        if (ld_v) V::template load<!STEADY, MAPPED>(vp, c.NK, t + VA, vr);
+        if (ld_k) next_k<!STEADY>(t + KA);
+        if (ld_v) next_v<!STEADY>(t + VA);
         const int na = STEADY ? 2 : nact(t);
         uint32_t pk[16];
         if (na > 0) {
@@ -1221,8 +1304,8 @@ struct FusedAttn {
     __device__ __forceinline__ int vector_phase(int t, float* s, uint32_t* pk) {
         if (STEADY || t + 2 < n_tiles) P::commit_k(kr, kbuf(t + 2), guard);
         if (STEADY || t + 1 < n_tiles) V::commit(vr, vbuf(t + 1));
-        if (STEADY || t + 3 < n_tiles) P::template load_k<!STEADY, MAPPED>(kp, t + 3, kr);
-        if (STEADY || t + 2 < n_tiles) V::template load<!STEADY, MAPPED>(vp, c.NK, t + 2, vr);
+        if (STEADY || t + 3 < n_tiles) next_k<!STEADY>(t + 3);
+        if (STEADY || t + 2 < n_tiles) next_v<!STEADY>(t + 2);
         const int na = STEADY ? 2 : nact(t);
         if (na > 0) softmax<STEADY>(t, na, s, pk);
         return na;
@@ -1271,6 +1354,11 @@ struct FusedAttn {
             V::template load<true, MAPPED>(vp, c.NK, t_lo + 1, vr);
         }
         if (t_lo + 2 < n_tiles) P::template load_k<true, MAPPED>(kp, t_lo + 2, kr);
+        slot_bad = false;
+        if (any) {  // the first vector phase's K / V tiles
+            read_k_slots(t_lo + 3);
+            read_v_slots(t_lo + 2);
+        }
         P::load_q(a, c, qw0 + lq, logit_scale, q, guard);
         if (any) {
             P::commit_k(kr0, kbuf(t_lo), guard);
@@ -1319,6 +1407,7 @@ struct FusedAttn {
 
     // Normalised O (or the split-K partial) of the wave's rows.
     __device__ __forceinline__ void finish(const RunArgs& a) {
+        if (kAhead && slot_bad) atomicOr(a.status, 1);
         const bool gbad = guard.bad();
         if (DBG || qw0 >= c.S) {
             report_range(a, gbad);
@@ -1425,6 +1514,11 @@ struct FusedAttn {
         if (k1) P::template load_k<true, MAPPED>(kp, t_lo + 1, kr1);
         if (v1) V::template load<true, MAPPED>(vp, c.NK, t_lo + 1, vr1);
         if (k2) P::template load_k<true, MAPPED>(kp, t_lo + 2, kr2);
+        slot_bad = false;
+        if (any) {  // the first step's K / V tiles
+            read_k_slots(t_lo + KA);
+            read_v_slots(t_lo + VA);
+        }
         P::load_q(a, c, qw0 + lq, logit_scale, q, guard);
         if (any) {
             P::commit_k(kr, kbuf(t_lo), guard);
