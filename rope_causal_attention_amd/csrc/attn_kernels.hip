@@ -201,26 +201,48 @@ __device__ __forceinline__ float2* split_ml(const RunArgs& a, size_t row, int sp
 // reads a slot written here while the map is one-to-one over the keys):
 // by the workgroups of the first split and of the first query head of each
 // kv head, each writing the tokens of its own query rows.  A slot outside
-// [0, n_slots) is skipped and sets the status word.
+// [0, n_slots) is skipped and sets the status word.  Every load is issued
+// before the first store (the compiler cannot move a load above a store
+// that may alias it), so the copy costs one memory round trip, not one per
+// 16-byte piece a thread moves.
 template <int D, int BM, int NT>
-__device__ void store_chunk_rows(const RunArgs& a, const Ctx& c) {
+__device__ __forceinline__ void store_chunk_rows(const RunArgs& a, const Ctx& c) {
     if (c.split != 0 || c.hq % (a.n_heads / a.n_kv_heads) != 0) return;
     constexpr int kCh = D * 2 / 16;  // 16-byte pieces of a 2-byte-element row
-    const int rows = min(BM, c.S - c.q0);
+    constexpr int kPer = (BM * kCh + NT - 1) / NT;
+    const int n = min(BM, c.S - c.q0) * kCh;
     const int32_t* map = a.kv_map + static_cast<size_t>(c.b) * a.map_stride + c.off;
-    for (int idx = threadIdx.x; idx < rows * kCh; idx += NT) {
+    // The pieces in vector registers (arrays of them were placed in scratch
+    // and LDS memory before the loops were unrolled).
+    typedef uint32_t Pieces __attribute__((ext_vector_type(4 * kPer)));
+    typedef int Slots __attribute__((ext_vector_type(kPer)));
+    Pieces kx, vx;
+    Slots slot;
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {  // surplus pieces re-read the last one (n >= 1)
+        const int idx = min(static_cast<int>(threadIdx.x) + NT * p, n - 1);
         const int i = c.q0 + idx / kCh, ch = idx % kCh;
-        const int slot = map[i];
-        if (static_cast<unsigned>(slot) >= static_cast<unsigned>(a.n_slots)) {
+        const size_t src = kv_index(a, c, i, D) * 2 + 16 * ch;
+        slot[p] = map[i];
+        const uint4 kw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src);
+        const uint4 vw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src);
+        kx[4 * p] = kw.x, kx[4 * p + 1] = kw.y, kx[4 * p + 2] = kw.z, kx[4 * p + 3] = kw.w;
+        vx[4 * p] = vw.x, vx[4 * p + 1] = vw.y, vx[4 * p + 2] = vw.z, vx[4 * p + 3] = vw.w;
+    }
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+        const int idx = static_cast<int>(threadIdx.x) + NT * p;
+        if (idx >= n) continue;
+        const int ch = idx % kCh;
+        if (static_cast<unsigned>(slot[p]) >= static_cast<unsigned>(a.n_slots)) {
             if (ch == 0) atomicOr(a.status, 1);
             continue;
         }
-        const size_t src = kv_index(a, c, i, D) * 2 + 16 * ch;
-        const size_t dst = (static_cast<size_t>(slot) * a.n_kv_heads + c.hkv) * D * 2 + 16 * ch;
+        const size_t dst = (static_cast<size_t>(slot[p]) * a.n_kv_heads + c.hkv) * D * 2 + 16 * ch;
         *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k)) + dst) =
-            *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src);
+            make_uint4(kx[4 * p], kx[4 * p + 1], kx[4 * p + 2], kx[4 * p + 3]);
         *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v)) + dst) =
-            *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src);
+            make_uint4(vx[4 * p], vx[4 * p + 1], vx[4 * p + 2], vx[4 * p + 3]);
     }
 }
 
