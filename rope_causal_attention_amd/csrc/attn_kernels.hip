@@ -1043,28 +1043,39 @@ struct FusedAttn {
     f32x16 o[D / 32];
     float m_run, l_a, l_b;
     // kShift: the scores arrive shifted by b_run, subtracted by the Q.K^T
-    // products themselves (the C operand of the matrix-core path, the scaling
-    // FMA of the integer ones), so the softmax exponentiates them as they
-    // are.  b_run is 0 until the lane's first maximum is known, then m_run,
-    // which moves only when a tile's maximum passes it by more than the
-    // slack.  The shift rounds differently from a later subtraction, so it is
-    // chosen per head_dim and score type, never per schedule: every launch
-    // shape of one input type then gives the same bits (chunked, cached,
-    // packed and plain launches agree).  It holds 16 more registers, which
-    // every fp16 schedule at head_dim 128 has to spare; at 64 and 96 one of
-    // them would spill (the paired eight-wave 96, the two-workgroup four-wave
-    // 64), and so would the eight-wave integer ones.
-    static constexpr bool kShift = D == 128 && !P::kIntScores;
+    // products themselves (the C operand of the matrix-core path), so the
+    // softmax exponentiates them as they are instead of subtracting the
+    // running max from each.  b_run is 0 until the lane's first maximum is
+    // known, then m_run, which moves only when a tile's maximum passes it by
+    // more than the slack.  The shift rounds differently from a later
+    // subtraction, so it is chosen per score type, never per schedule or
+    // launch shape: every launch of one input type then gives the same bits
+    // (chunked, cached, packed and plain launches agree).  The integer paths
+    // subtract after their scaling FMA (their eight-wave kernels have no
+    // registers for it).  At head_dim 128 the 16 entries of -b_run stay in
+    // registers, which every fp16 schedule there has to spare; at 64 and 96
+    // they would spill (the paired eight-wave 96, the two-workgroup four-wave
+    // 64), so there the entries are written afresh before each product (a
+    // few register moves per 32-key block, against 32 subtractions per tile).
+    static constexpr bool kShift = !P::kIntScores;
+    static constexpr bool kKeepShift = kShift && D == 128;
     float b_run;
-    f32x16 nbias;  // -b_run in every entry
+    f32x16 nbias;  // kKeepShift: -b_run in every entry
     __device__ __forceinline__ void set_shift(float b) {
         b_run = kShift ? b : 0.f;
+        if constexpr (kKeepShift) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) nbias[v] = -b_run;
+            for (int v = 0; v < 16; ++v) nbias[v] = -b_run;
+        }
     }
     __device__ __forceinline__ f32x16 score_shift() const {
-        if constexpr (kShift) return nbias;
-        return f32x16{};
+        if constexpr (kKeepShift) return nbias;
+        f32x16 r = {};
+        if constexpr (kShift) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) r[v] = -b_run;
+        }
+        return r;
     }
     // exp2 argument of a (shifted) score
     __device__ __forceinline__ float exp_arg(float x) const { return kShift ? x : x - m_run; }
