@@ -300,6 +300,56 @@ def test_bad_slot_is_read_as_slot_zero_and_reported():
         attn.close()
 
 
+# name, B, Hq, Hkv, D, dtype, prefix, S, n_split: the four-wave kernels (bf16 and
+# int16), the paired eight-wave kernel at head_dim 96, the two-group one at 128
+# (heads packed four to a workgroup), and an eight-wave split launch
+DEEP_BAD = [
+    ("deep_bad_4wave_d64", 1, 2, 2, 64, "bf16", 1100, 40, 1),
+    ("deep_bad_4wave_i16_d64", 1, 2, 2, 64, "i16", 1100, 40, 1),
+    ("deep_bad_8wave_d96", 8, 32, 32, 96, "bf16", 1100, 256, 1),
+    ("deep_bad_8wave_d128", 8, 32, 8, 128, "bf16", 1100, 256, 1),
+    ("deep_bad_split_d96", 1, 32, 32, 96, "bf16", 1100, 256, 8),
+]
+
+
+@pytest.mark.parametrize("case", DEEP_BAD, ids=[c[0] for c in DEEP_BAD])
+def test_bad_slots_deep_in_the_prefix_read_slot_zero(case):
+    """Map entries outside the cache at keys that the key loop (not the
+    prologue) stages, in the prefix and in the chunk: the run reads slot 0 for
+    them and reports the range error, so its O equals bit for bit that of a
+    run whose map holds slot 0 at those keys (which reports nothing)."""
+    name, B, Hq, Hkv, D, dt, prefix, S, n_split = case
+    width = prefix + S
+    n_slots = B * ((width + 63) // 64) * 64 + 64
+    c = Case(name, B, Hq, Hkv, D, dt, 1e4, [prefix] * B, S, "paged", n_slots)
+    announce(c.name, "n_split", n_split)
+    bad, zero = c.map.copy(), c.map.copy()
+    keys = [5, 700, 701, prefix - 1, prefix + 10]
+    for i, j in enumerate(keys):
+        bad[B - 1, j] = n_slots + i if i % 2 == 0 else -1 - i
+        zero[B - 1, j] = 0
+    attn = _handle(c)
+    try:
+        off = torch.tensor(c.prefix, dtype=torch.int32, device="cuda")
+        qd, kcd, vcd = c.q.cuda(), c.kc.cuda(), c.vc.cuda()
+        ws = None
+        if n_split > 1:
+            ws = torch.empty(pa.prefill_attn_run_cached_workspace_size(attn.handle, B, S, n_split),
+                             dtype=torch.uint8, device="cuda")
+        outs, codes = [], []
+        for m in (bad, zero):
+            o = attn.run_cached(qd, kcd, vcd, torch.from_numpy(m).cuda(), pos_offsets=off, score_scale=c.scale,
+                                n_split=n_split, workspace=ws)
+            torch.cuda.synchronize()
+            codes.append(attn.status())
+            outs.append(o.cpu())
+    finally:
+        attn.close()
+    assert codes == [pa.PA_ERANGE, pa.PA_OK], codes
+    assert torch.isfinite(outs[0]).all()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_chunk_past_the_map_row_zeroes_that_sequence():
     c = Case("short_map", 2, 2, 1, 64, "bf16", 1e4, [10, 20], 40, "paged", 512)
     announce(c.name)
