@@ -47,12 +47,19 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float row_sum16(float x) {
-    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-    x += dpp<0x141>(x);  // row_half_mirror: the other quad of the half row
-    x += dpp<0x140>(x);  // row_mirror: the other half of the row
-    return x;
+// N independent sums reduced in lockstep: each DPP step reads a value written
+// N instructions earlier, so the steps need no wait states between them (one
+// chain at a time, each step waits for the one before).
+template <int N>
+__device__ __forceinline__ void row_sum16(float (&x)[N]) {
+#pragma unroll
+    for (int g = 0; g < N; ++g) x[g] += dpp<0xB1>(x[g]);   // quad_perm [1,0,3,2]
+#pragma unroll
+    for (int g = 0; g < N; ++g) x[g] += dpp<0x4E>(x[g]);   // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int g = 0; g < N; ++g) x[g] += dpp<0x141>(x[g]);  // row_half_mirror: the other quad of the half row
+#pragma unroll
+    for (int g = 0; g < N; ++g) x[g] += dpp<0x140>(x[g]);  // row_mirror: the other half of the row
 }
 
 // Combine the same lane position of the four 16-lane rows.
@@ -198,52 +205,56 @@ __global__ __launch_bounds__(kThreads, G >= 8 ? 2 : 4) void decode_kernel(Decode
         }
         __syncthreads();
 
-        int j = s0 + my;
-        Raw<E, F32> kr, vr;
-        {
-            const size_t r = static_cast<size_t>(smap[min(j, s1 - 1) - s0]) * row_elems + head_off;
-            kr.load(a.k, r);
-            vr.load(a.v, r);
-        }
-        for (int j0 = s0; j0 < s1; j0 += kKeysPerStep) {
-            const int jn = j0 + kKeysPerStep + my;
-            const bool more = j0 + kKeysPerStep < s1;
-            Raw<E, F32> kn, vn;
-            if (more) {
-                const size_t r = static_cast<size_t>(smap[min(jn, s1 - 1) - s0]) * row_elems + head_off;
+        // One step: key j of this row from (kc, vc) while the rows of the next
+        // step go to (kn, vn).  The loop below runs two steps per iteration
+        // with the register sets swapped, so no step copies the next rows.
+        auto step = [&](int j0, int j, const Raw<E, F32>& kc, const Raw<E, F32>& vc, Raw<E, F32>& kn,
+                        Raw<E, F32>& vn) {
+            if (j0 + kKeysPerStep < s1) {
+                const size_t r = static_cast<size_t>(smap[min(j + kKeysPerStep, s1 - 1) - s0]) * row_elems + head_off;
                 kn.load(a.k, r);
                 vn.load(a.v, r);
             }
             const bool valid = j < s1;
             float kx[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) kx[e] = kr.at(e);
+            for (int e = 0; e < E; ++e) kx[e] = kc.at(e);
             rotate<E>(kx, a.rope_f32 + static_cast<size_t>(min(j, s1 - 1)) * D + sub * E);
+            float sc[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                float sc = 0.f;
+                sc[g] = 0.f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) sc = fmaf(q[g][e], kx[e], sc);
-                sc = row_sum16(sc);
-                const bool need = valid && sc > m[g] + kSlack;
+                for (int e = 0; e < E; ++e) sc[g] = fmaf(q[g][e], kx[e], sc[g]);
+            }
+            row_sum16(sc);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const bool need = valid && sc[g] > m[g] + kSlack;
                 if (__builtin_amdgcn_ballot_w64(need)) {
-                    const float m_new = need ? sc : m[g];
+                    const float m_new = need ? sc[g] : m[g];
                     const float alpha = weight(m[g], m_new);
                     m[g] = m_new;
                     l[g] *= alpha;
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
                 }
-                const float p = valid ? __builtin_amdgcn_exp2f(sc - m[g]) : 0.f;
+                const float p = valid ? __builtin_amdgcn_exp2f(sc[g] - m[g]) : 0.f;
                 l[g] += p;
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p, vr.at(e), acc[g][e]);
+                for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p, vc.at(e), acc[g][e]);
             }
-            j = jn;
-            if (more) {
-                kr = kn;
-                vr = vn;
-            }
+        };
+        Raw<E, F32> k0, v0, k1, v1;
+        {
+            const size_t r = static_cast<size_t>(smap[min(s0 + my, s1 - 1) - s0]) * row_elems + head_off;
+            k0.load(a.k, r);
+            v0.load(a.v, r);
+        }
+        for (int j0 = s0; j0 < s1; j0 += 2 * kKeysPerStep) {
+            step(j0, j0 + my, k0, v0, k1, v1);
+            if (j0 + kKeysPerStep >= s1) break;
+            step(j0 + kKeysPerStep, j0 + kKeysPerStep + my, k1, v1, k0, v0);
         }
     }
 
