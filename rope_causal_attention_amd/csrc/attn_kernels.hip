@@ -513,8 +513,16 @@ struct I16QK {
     using Guard = DigitGuard;
 
     // Fixed-point rotation with round-half-up: (x C - y S + 2^13) >> 14, (x S + y C + 2^13) >> 14.
-    __device__ static __forceinline__ int rot_x(int x, int y, int C, int S) { return (x * C - y * S + 8192) >> 14; }
-    __device__ static __forceinline__ int rot_y(int x, int y, int C, int S) { return (x * S + y * C + 8192) >> 14; }
+    // Every operand is an int16 value or a Q1.14 entry (|C|, |S| <= 2^14), so
+    // the 24-bit multiplies (full rate) are exact: |product| <= 2^29.  Spelled
+    // out because the compiler cannot see that range for the in-kernel
+    // quantisation codes and falls back to the quarter-rate 32-bit multiply.
+    __device__ static __forceinline__ int rot_x(int x, int y, int C, int S) {
+        return (__mul24(x, C) - __mul24(y, S) + 8192) >> 14;
+    }
+    __device__ static __forceinline__ int rot_y(int x, int y, int C, int S) {
+        return (__mul24(x, S) + __mul24(y, C) + 8192) >> 14;
+    }
 
     // a = 128 h + l, l in [-64, 63]; returns the three digit bytes h, l, h + l
     // (all three are int8 for a in [-8383, 8382]: at 8383, h + l = 65 + 63 wraps).
