@@ -13,7 +13,10 @@ checked for the hazards a wrong bound would cause on the GPU:
   * the unmasked (steady) softmax and score tiles lie wholly below every row
     of the block;
   * both wave groups of the two-group schedule pass the same number of
-    barriers, and every tile of the range is scored and multiplied once.
+    barriers, and every tile of the range is scored and multiplied once;
+  * cached launches read the index-map entries of the next K and V tiles one
+    step ahead: every pipelined tile load must find the entries of that very
+    tile in hand (read in the prologue or by the load of the tile before).
 
 Schedules (constants as in the kernel): plain (2 buffers, K staged 2 tiles and
 V 1 tile ahead, one barrier per tile), PAIR (4 buffers, 3 and 2 ahead, one
@@ -39,8 +42,9 @@ SCHEDULES = {
 
 
 class Replay:
-    def __init__(self, sched, kshift, S, q0, bmp, n_split=1, split=0):
+    def __init__(self, sched, kshift, S, q0, bmp, n_split=1, split=0, ahead_skew=0):
         self.sched = sched
+        self.ahead_skew = ahead_skew  # tests only: a wrong first read-ahead tile
         self.bufs, self.KA, self.VA, self.pair, self.pp = SCHEDULES[sched]
         self.NK = kshift + S
         self.n_all = math.ceil((kshift + min(q0 + bmp, S)) / BN)
@@ -58,6 +62,17 @@ class Replay:
         self.barriers = {}
         self.scored = {}  # group -> tiles read from the K buffers by Q.K^T
         self.multiplied = {}
+        self.ahead = {}   # (group, "K"/"V") -> tile whose map entries are held
+
+    # --- map entries read ahead (cached launches)
+    def _read_ahead(self, g, kind, t):
+        self.ahead[(g, kind)] = t
+
+    def _pipelined_load(self, g, kind, t, clamped):
+        held = self.ahead.get((g, kind))
+        assert held == t, f"{self.sched}: {kind} load of tile {t} with the map entries of tile {held}"
+        self._load(t, clamped)
+        self._read_ahead(g, kind, t + 1)
 
     def slot(self, t):
         if self.pp:
@@ -93,6 +108,8 @@ class Replay:
         for t, on in ((t_lo + 1, k1), (t_lo + 1, v1), (t_lo + 2, k2)):
             if on:
                 self._load(t, True)
+        self._read_ahead(g, "K", t_lo + KA + self.ahead_skew)
+        self._read_ahead(g, "V", t_lo + VA)
         self._rw(e, g, "w", "K", t_lo)
         self._rw(e, g, "w", "V", t_lo)
         if k1:
@@ -112,9 +129,9 @@ class Replay:
             ld_k = steady or t + KA < n
             ld_v = steady or t + VA < n
             if ld_k:
-                self._load(t + KA, not steady)
+                self._pipelined_load(g, "K", t + KA, not steady)
             if ld_v:
-                self._load(t + VA, not steady)
+                self._pipelined_load(g, "V", t + VA, not steady)
             if steady:
                 self.full.append(t)
             if steady or t + 1 < n:
@@ -158,6 +175,8 @@ class Replay:
         if t_lo + 2 < n:
             self._load(t_lo + 2, True)
             regs["K"] = t_lo + 2
+        self._read_ahead(g, "K", t_lo + 3 + self.ahead_skew)
+        self._read_ahead(g, "V", t_lo + 2)
         self._rw(e, g, "w", "K", t_lo)
         self._rw(e, g, "w", "V", t_lo)
         if t_lo + 1 < n:
@@ -177,10 +196,10 @@ class Replay:
                 assert regs["V"] == t + 1, ("V registers", regs["V"], t + 1)
                 self._rw(e, g, "w", "V", t + 1)
             if steady or t + 3 < n:
-                self._load(t + 3, not steady)
+                self._pipelined_load(g, "K", t + 3, not steady)
                 regs["K"] = t + 3
             if steady or t + 2 < n:
-                self._load(t + 2, not steady)
+                self._pipelined_load(g, "V", t + 2, not steady)
                 regs["V"] = t + 2
             if steady:
                 self.full.append(t)
@@ -308,3 +327,7 @@ def test_replay_detects_a_wrong_bound():
             Replay("plain", 0, 1000, 768, 128).run().check()
     finally:
         SCHEDULES["plain"] = saved
+    for sched in SCHEDULES:  # a first read-ahead one tile off
+        with pytest.raises(AssertionError):
+            for kshift, S, q0 in _blocks(256, [1000], [0]):
+                Replay(sched, kshift, S, q0, 256, ahead_skew=-1).run().check()
