@@ -331,3 +331,31 @@ def test_replay_detects_a_wrong_bound():
         with pytest.raises(AssertionError):
             for kshift, S, q0 in _blocks(256, [1000], [0]):
                 Replay(sched, kshift, S, q0, 256, ahead_skew=-1).run().check()
+
+
+def test_replay_constants_match_the_kernel_source():
+    """The replay's schedule table restates the kernel's constants; a change to
+    either one alone must fail here (the replay would otherwise keep checking
+    a schedule the kernel no longer runs)."""
+    import pathlib
+    import re
+    src = (pathlib.Path(__file__).resolve().parents[1] / "rope_causal_attention_amd" / "csrc" /
+           "attn_kernels.hip").read_text()
+
+    def ternary(name):
+        m = re.search(r"static constexpr int " + name + r" = (.+?);", src)
+        assert m, name
+        return m.group(1).replace(" ", "")
+
+    assert ternary("kBufs") == "PP?3:(PAIR?4:2)"
+    assert ternary("KA") == "PAIR?3:2"
+    assert ternary("VA") == "PAIR?2:1"
+    m = re.search(r"constexpr int kMinSplitTiles = (\d+);", src)
+    assert m and int(m.group(1)) == K_MIN_SPLIT_TILES
+    # the table: (buffers, K ahead, V ahead) of each schedule, from the same expressions
+    pp, pair, plain = SCHEDULES["pp"], SCHEDULES["pair"], SCHEDULES["plain"]
+    assert (plain[0], plain[1], plain[2]) == (2, 2, 1)
+    assert (pair[0], pair[1], pair[2]) == (4, 3, 2)
+    assert pp[0] == 3
+    # the two-group schedule's look-ahead is spelled out in its phases: K(t+3), V(t+2)
+    assert "next_k<!STEADY>(t + 3)" in src and "next_v<!STEADY>(t + 2)" in src
