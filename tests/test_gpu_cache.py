@@ -503,6 +503,7 @@ FUSED_CASES = [
     # name, B, Hq, Hkv, D, dtype (bf16q: bf16 quantised in-kernel), chunks, layout, n_split
     ("fu_bf16_d96_8wave", 1, 32, 32, 96, "bf16", [1024, 1024, 512], "ring", 0),
     ("fu_bf16_d128_gqa_split", 2, 16, 4, 128, "bf16", [300, 700, 64], "paged", 4),
+    ("fu_bf16_d96_gqa2_8wave", 2, 32, 16, 96, "bf16", [300, 77, 513], "ring", 0),  # two heads per workgroup
     ("fu_bf16_d64_4wave", 2, 4, 2, 64, "bf16", [100, 333, 1, 250], "paged", 1),
     ("fu_i16_d128", 1, 8, 2, 128, "i16", [200, 456], "ring", 1),
     ("fu_i16_d128_split", 1, 8, 2, 128, "i16", [512, 300], "paged", 3),
