@@ -143,6 +143,8 @@ PLAIN_CASES = [
     ("same_bf16_4wave", 1, 4, 2, 300, 128, "bf16", 1e4),
     ("same_bf16_8wave", 1, 64, 8, 1030, 96, "bf16", 1e4),
     ("same_bf16_8wave_paired", 1, 64, 8, 2000, 96, "bf16", 1e4),  # 256 pairs of query blocks
+    ("same_bf16_8wave_d64", 1, 64, 64, 1030, 64, "bf16", 1e4),  # one head per workgroup
+    ("same_bf16_8wave_d128", 1, 64, 16, 1030, 128, "bf16", 1e4),  # two-group schedule, four heads packed
     ("same_f32", 1, 2, 1, 200, 64, "f32", 1e4),
     ("same_i16", 1, 4, 4, 300, 128, "i16", 1e4),
 ]
