@@ -60,9 +60,11 @@ enum prefill_attn_dtype {
                        values below 2^-14 keep fewer bits (fp16 subnormals).  A larger K' or a non-finite O
                        sets the status word (PA_EOVERFLOW from prefill_attn_status). */
     PA_IN_I16 = 2,  /* Q, K int16 fixed point, V bfloat16; integer RoPE, exact int32 scores, fp32 softmax.
-                       Range: every rotated Q'/K' value must lie in [-8383, 8382] (the int8 digit split of
-                       the scores; |x| <= 5900 for every input is enough); outside it the scores are wrong
-                       and the status word is set (PA_EOVERFLOW).  V as for PA_IN_BF16. */
+                       Range: every rotated Q'/K' value must lie in [-16448, 16319] (the int8 digit split
+                       of the scores; |x| <= 11500 for every input is enough); outside it the scores are
+                       wrong and the status word is set (PA_EOVERFLOW).  Every score Q'.K' must also fit
+                       int32, or it wraps unreported (|x| <= 2895 for every input is enough at head_dim
+                       128).  V as for PA_IN_BF16. */
     PA_IN_BF16_Q16 = 3, /* Q, K, V bfloat16; each (token, head) row of Q and K quantised inside the kernel to
                           int16 codes, round-half-even(x * 2047 / max|x|) in fp32 (the 2kiu.com retelling, §3.3:
                           per-token dynamic activation scale), then the PA_IN_I16 path with
@@ -87,7 +89,7 @@ enum prefill_attn_status {
     PA_EOVERFLOW = -7 /* a run saw a value outside the range its kernel computes in: a non-finite
                          O (bf16 path: an fp16 operand overflowed, or an input was not finite) or an
                          fp16 K' = RoPE(K) beyond 65504, or (int16 path) a rotated Q'/K' value outside
-                         [-8383, 8382], where the int8 digit split wraps; O is not valid */
+                         [-16448, 16319], where the int8 digit split wraps; O is not valid */
 };
 
 /*
@@ -345,7 +347,7 @@ int prefill_attn_rope_table_q14(int max_seq, int head_dim, double rope_theta, in
  *     "手写内核实现6倍prefill加速", §3.1, with Q1.14 tables), formed by the K staging
  *     of the int16 kernels (table addressing, rotation, digit split into LDS) with
  *     the staging width a prefill of this shape uses, and read back as 128 h + l
- *     from the digit planes.  Values outside [-8383, 8382] set the status word
+ *     from the digit planes.  Values outside [-16448, 16319] set the status word
  *     (PA_EOVERFLOW) and come back wrong.
  *   prefill_attn_debug_scores_i32: the int32 scores of the causal part,
  *     scores[b][h][i][j] = Q'[b,i,h] . K'[b,j,kvh(h)] for j <= i, of

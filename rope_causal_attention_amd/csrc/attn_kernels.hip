@@ -36,8 +36,9 @@
 //    pairs are split over the 8 XCDs so one head's K/V stays in one L2.
 //  * int16 variant: Q'/K' rotated in integers, split into signed 8-bit digits
 //    a = 128 h + l (l in [-64, 63], h in [-23, 23] for |a| <= 2897), and the
-//    exact int32 score is recombined from three v_mfma_i32_32x32x32_i8
-//    products (hh, ll and (h+l)(h+l)); P.V as in the bf16 kernel.
+//    exact int32 score is recombined from the v_mfma_i32_32x32x32_i8
+//    products hh, ll and hl + lh (the two cross products share one
+//    accumulator); P.V as in the bf16 kernel.
 //  * fp32 variant: v_mfma_f32_32x32x2_f32 for both products, fp32 LDS tiles.
 
 #include <hip/hip_runtime.h>
@@ -353,7 +354,6 @@ struct Bf16QK {
     static constexpr int kStride = D + 8;  // f16 per K' row (16-byte pad against bank conflicts)
     static constexpr bool kSerialBlocks = false;  // the two key blocks' MFMAs may interleave
     static constexpr bool kIntScores = false;
-    static constexpr bool kSlotsAhead = true;  // room for the mapped launches' slot offsets
     static constexpr int kBytes = BN * kStride * 2;
     static constexpr int kChunks = BN * D / 8;  // 16-byte chunks per K tile
     static constexpr int kPer = (kChunks + NT - 1) / NT;
@@ -491,13 +491,12 @@ struct I16QK {
     // within their register budget.
     static constexpr bool kSerialBlocks = true;
     static constexpr bool kIntScores = true;
-    static constexpr bool kSlotsAhead = true;
     static constexpr int kPlane = BN * kRow;
-    static constexpr int kBytes = 3 * kPlane;  // planes: high digit, low digit, high + low
+    static constexpr int kBytes = 2 * kPlane;  // planes: high digit, low digit
     static constexpr int kChunks = BN * D / 8;
     static constexpr int kPer = (kChunks + NT - 1) / NT;
     struct Q {
-        i32x4 h[D / 32], l[D / 32], m[D / 32];
+        i32x4 h[D / 32], l[D / 32];
         float scale;
     };
     struct KRegs {
@@ -524,41 +523,38 @@ struct I16QK {
         return (__mul24(x, S) + __mul24(y, C) + 8192) >> 14;
     }
 
-    // a = 128 h + l, l in [-64, 63]; returns the three digit bytes h, l, h + l
-    // (all three are int8 for a in [-8383, 8382]: at 8383, h + l = 65 + 63 wraps).
-    __device__ static __forceinline__ void split(int a, uint32_t& h, uint32_t& l, uint32_t& m) {
+    // a = 128 h + l, l in [-64, 63]; returns the digit bytes h and l (both
+    // int8 for a in [-16448, 16319]: at 16320, h = 128 wraps).
+    __device__ static __forceinline__ void split(int a, uint32_t& h, uint32_t& l) {
         const int lo = ((a + 64) & 127) - 64;
         const int hi = (a - lo) >> 7;
         h = static_cast<uint32_t>(hi) & 0xffu;
         l = static_cast<uint32_t>(lo) & 0xffu;
-        m = static_cast<uint32_t>(hi + lo) & 0xffu;
     }
 
     // Rotate 4 pairs (one uint4 of int16) with 4 (C, S) pairs and split into digits:
     // 8 bytes per plane returned as two dwords each; the guard sees the rotated values.
     template <class G>
     __device__ static __forceinline__ void rotate_split8(const uint4& raw, const uint4& cs, uint2& h, uint2& l,
-                                                         uint2& m, G& g) {
+                                                         G& g) {
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
         const uint32_t t[4] = {cs.x, cs.y, cs.z, cs.w};
-        uint32_t hb[2] = {0, 0}, lb[2] = {0, 0}, mb[2] = {0, 0};
+        uint32_t hb[2] = {0, 0}, lb[2] = {0, 0};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int x = i16_lo(w[j]), y = i16_hi(w[j]);
             const int C = i16_lo(t[j]), S = i16_hi(t[j]);
             const int xr = rot_x(x, y, C, S), yr = rot_y(x, y, C, S);
             g.add(xr, yr);
-            uint32_t a0, a1, a2, b0, b1, b2;
-            split(xr, a0, a1, a2);
-            split(yr, b0, b1, b2);
+            uint32_t a0, a1, b0, b1;
+            split(xr, a0, a1);
+            split(yr, b0, b1);
             const int sh = 16 * (j & 1);
             hb[j >> 1] |= (a0 | (b0 << 8)) << sh;
             lb[j >> 1] |= (a1 | (b1 << 8)) << sh;
-            mb[j >> 1] |= (a2 | (b2 << 8)) << sh;
         }
         h = make_uint2(hb[0], hb[1]);
         l = make_uint2(lb[0], lb[1]);
-        m = make_uint2(mb[0], mb[1]);
     }
 
     template <bool MAPPED>
@@ -577,7 +573,7 @@ struct I16QK {
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
             const int d0 = 32 * ks + 16 * lh;
-            uint2 h[2], l[2], m[2];
+            uint2 h[2], l[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 uint4 raw = make_uint4(0, 0, 0, 0), cs = raw;
@@ -585,11 +581,10 @@ struct I16QK {
                     raw = ld16(rq.base, qi * rq.stride + 2 * (d0 + 8 * half));
                     cs = ld16(tab, (qi * D + d0 + 8 * half) * 2);
                 }
-                rotate_split8(raw, cs, h[half], l[half], m[half], g);
+                rotate_split8(raw, cs, h[half], l[half], g);
             }
             q.h[ks] = i32x4{(int)h[0].x, (int)h[0].y, (int)h[1].x, (int)h[1].y};
             q.l[ks] = i32x4{(int)l[0].x, (int)l[0].y, (int)l[1].x, (int)l[1].y};
-            q.m[ks] = i32x4{(int)m[0].x, (int)m[0].y, (int)m[1].x, (int)m[1].y};
         }
     }
 
@@ -620,33 +615,31 @@ struct I16QK {
             if (!has(i)) continue;
             const int idx = static_cast<int>(threadIdx.x % NT) + NT * i;
             const int row = idx / (D / 8), ch = idx % (D / 8);
-            uint2 h, l, m;
-            rotate_split8(r.raw[i], r.cs[i], h, l, m, g);
+            uint2 h, l;
+            rotate_split8(r.raw[i], r.cs[i], h, l, g);
             char* p = lds + row * kRow + 8 * ch;
             *reinterpret_cast<uint2*>(p) = h;
             *reinterpret_cast<uint2*>(p + kPlane) = l;
-            *reinterpret_cast<uint2*>(p + 2 * kPlane) = m;
         }
     }
 
-    // Exact int32 scores S^T for key block kb: 2^14 hh + 2^7 (mm - hh - ll) + ll.
+    // Exact int32 scores S^T for key block kb: 2^14 hh + 2^7 (hl + lh) + ll.
     __device__ static __forceinline__ void qk_i32(const char* lds, int kb, const Q& q, int* s, int lq, int lh) {
         const char* row = lds + (32 * kb + lq) * kRow + 16 * lh;
-        i32x16 hh = {}, ll = {}, mm = {};
+        i32x16 hh = {}, ll = {}, x = {};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
             const i32x4 ah = *reinterpret_cast<const i32x4*>(row + 32 * ks);
             const i32x4 al = *reinterpret_cast<const i32x4*>(row + kPlane + 32 * ks);
-            const i32x4 am = *reinterpret_cast<const i32x4*>(row + 2 * kPlane + 32 * ks);
             hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah, q.h[ks], hh, 0, 0, 0);
             ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(al, q.l[ks], ll, 0, 0, 0);
-            mm = __builtin_amdgcn_mfma_i32_32x32x32_i8(am, q.m[ks], mm, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah, q.l[ks], x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(al, q.h[ks], x, 0, 0, 0);
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const uint32_t h = static_cast<uint32_t>(hh[v]), l = static_cast<uint32_t>(ll[v]);
-            const uint32_t m = static_cast<uint32_t>(mm[v]);
-            s[v] = static_cast<int>((h << 14) + ((m - h - l) << 7) + l);
+            s[v] = static_cast<int>((h << 14) + (static_cast<uint32_t>(x[v]) << 7) + l);
         }
     }
 
@@ -683,7 +676,7 @@ __device__ __forceinline__ float newton_reciprocal(float l) {
 // even, all in fp32, so every workgroup that stages a row derives the same
 // codes; the MNN-on-K3 blog (§四) fuses the absmax scan with the quantise
 // step, done here while the row is in registers.  The codes then take the
-// int16 path (integer RoPE, three-digit exact int32 scores); the logit is
+// int16 path (integer RoPE, two-digit exact int32 scores); the logit is
 // s * score_scale * (m_q / 2047) * (m_k / 2047).
 __device__ __forceinline__ float quant_scale(float m) { return m > 0.f ? 2047.0f / m : 0.f; }
 __device__ __forceinline__ int quant_code(float x, float scale) {
@@ -706,8 +699,8 @@ struct I16QuantQK : I16QK<D, NT> {
     using Base = I16QK<D, NT>;
     static constexpr int kRow = Base::kRow;
     static constexpr int kPlane = Base::kPlane;
-    static constexpr int kInv = 3 * kPlane;            // 64 floats: m_k / 2047 of each key row
-    static constexpr int kBytes = 3 * kPlane + BN * 4;
+    static constexpr int kInv = 2 * kPlane;            // 64 floats: m_k / 2047 of each key row
+    static constexpr int kBytes = 2 * kPlane + BN * 4;
     static constexpr int E = D / 16;                   // elements of a key row per lane (16 lanes per row)
     static constexpr int kPasses = BN * 16 / NT;       // rows per thread per tile
     static_assert(BN * 16 % NT == 0, "whole passes");
@@ -715,9 +708,6 @@ struct I16QuantQK : I16QK<D, NT> {
     using KPtr = typename Base::KPtr;
     // Codes in [-2048, 2047] rotate to at most 2897 in magnitude: always exact.
     using Guard = NoGuard;
-    // At head_dim 128 the four-wave kernel has no registers for the slot
-    // offsets of its 8 K / V rows (they spilled).
-    static constexpr bool kSlotsAhead = D < 128;
     struct KRegs {
         uint32_t raw[kPasses][E / 2];  // bf16 pairs
         uint32_t cs[kPasses][E / 2];   // Q1.14 (C, S) pairs
@@ -754,7 +744,7 @@ struct I16QuantQK : I16QK<D, NT> {
         q.scale = scale * (m / 2047.0f);
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-            uint2 h[2], l[2], mm[2];
+            uint2 h[2], l[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const uint32_t w[4] = {raw[ks][half].x, raw[ks][half].y, raw[ks][half].z, raw[ks][half].w};
@@ -763,12 +753,10 @@ struct I16QuantQK : I16QK<D, NT> {
                 for (int j = 0; j < 4; ++j)
                     cw[j] = (static_cast<uint32_t>(quant_code(bf_lo(w[j]), qs)) & 0xffffu) |
                             (static_cast<uint32_t>(quant_code(bf_hi(w[j]), qs)) << 16);
-                Base::rotate_split8(make_uint4(cw[0], cw[1], cw[2], cw[3]), cs[ks][half], h[half], l[half], mm[half],
-                                    g);
+                Base::rotate_split8(make_uint4(cw[0], cw[1], cw[2], cw[3]), cs[ks][half], h[half], l[half], g);
             }
             q.h[ks] = i32x4{(int)h[0].x, (int)h[0].y, (int)h[1].x, (int)h[1].y};
             q.l[ks] = i32x4{(int)l[0].x, (int)l[0].y, (int)l[1].x, (int)l[1].y};
-            q.m[ks] = i32x4{(int)mm[0].x, (int)mm[0].y, (int)mm[1].x, (int)mm[1].y};
         }
     }
 
@@ -806,23 +794,22 @@ struct I16QuantQK : I16QK<D, NT> {
             for (int e = 0; e < E / 2; ++e) m = fmaxf(m, fmaxf(fabsf(bf_lo(r.raw[i][e])), fabsf(bf_hi(r.raw[i][e]))));
             m = row_max16(m);
             const float ks = quant_scale(m);
-            uint32_t hb[E / 4 + 1] = {}, lb[E / 4 + 1] = {}, mb[E / 4 + 1] = {};
+            uint32_t hb[E / 4 + 1] = {}, lb[E / 4 + 1] = {};
 #pragma unroll
             for (int e = 0; e < E / 2; ++e) {
                 const int x = quant_code(bf_lo(r.raw[i][e]), ks), y = quant_code(bf_hi(r.raw[i][e]), ks);
                 const int C = i16_lo(r.cs[i][e]), S = i16_hi(r.cs[i][e]);
-                uint32_t a0, a1, a2, b0, b1, b2;
-                Base::split(Base::rot_x(x, y, C, S), a0, a1, a2);
-                Base::split(Base::rot_y(x, y, C, S), b0, b1, b2);
+                uint32_t a0, a1, b0, b1;
+                Base::split(Base::rot_x(x, y, C, S), a0, a1);
+                Base::split(Base::rot_y(x, y, C, S), b0, b1);
                 const int sh = 16 * (e & 1);
                 hb[e >> 1] |= (a0 | (b0 << 8)) << sh;
                 lb[e >> 1] |= (a1 | (b1 << 8)) << sh;
-                mb[e >> 1] |= (a2 | (b2 << 8)) << sh;
             }
             char* pr = lds + row * kRow + E * sub;
 #pragma unroll
-            for (int pl = 0; pl < 3; ++pl) {
-                const uint32_t* w = pl == 0 ? hb : pl == 1 ? lb : mb;
+            for (int pl = 0; pl < 2; ++pl) {
+                const uint32_t* w = pl == 0 ? hb : lb;
                 char* dst = pr + pl * kPlane;
                 if (E == 8) {
                     *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
@@ -1021,9 +1008,8 @@ struct FusedAttn {
     // to stage, read one step before their loads so that a load does not wait
     // for its map entry (without them every step waited for the map reads
     // before its tile loads: the cached launches ran 20-60% slower than plain
-    // ones).  They take P::kRows + V::kRows registers; a policy without them
-    // to spare (P::kSlotsAhead false) reads each row's entry just before it.
-    static constexpr bool kAhead = MAPPED && P::kSlotsAhead;
+    // ones).  They take P::kRows + V::kRows registers.
+    static constexpr bool kAhead = MAPPED;
     uint32_t km[kAhead ? P::kRows : 1], vm[kAhead ? V::kRows : 1];
     bool slot_bad;  // a slot read ahead was outside the cache (reported by finish)
     __device__ __forceinline__ void read_k_slots(int tile) {
@@ -1840,7 +1826,7 @@ __global__ __launch_bounds__(kThreads) void kv_cache_update_kernel(RunArgs a, ui
 // RoPE of int16 rows through the int16 path's own K staging: a workgroup of
 // NT threads (the NT of the prefill launch of this shape) loads one 64-row tile
 // of one (batch, head) with its Q1.14 table rows (load_k), rotates it and
-// splits it into the three digit planes in LDS (commit_k, rotate_split8), and
+// splits it into the two digit planes in LDS (commit_k, rotate_split8), and
 // writes back x' = 128 h + l read from the planes.  a.k is the input,
 // a.n_kv_heads its head count.
 template <int D, int NT>

@@ -63,9 +63,9 @@ struct F16Guard {
     }
     __device__ __forceinline__ bool bad() const { return (m & 0xffffu) >= 0x7c00u || (m >> 16) >= 0x7c00u; }
 };
-// Rotated int16 values split into int8 digits h, l and h + l (a = 128 h + l,
-// l in [-64, 63]): all three fit int8 for every a in [-8383, 8382].
-constexpr int kDigitMax = 8382, kDigitMin = -8383;
+// Rotated int16 values split into int8 digits h and l (a = 128 h + l,
+// l in [-64, 63]): both fit int8 for every a in [-16448, 16319].
+constexpr int kDigitMax = 16319, kDigitMin = -16448;
 struct DigitGuard {
     int mx = 0, mn = 0;
     __device__ __forceinline__ void add(int a, int b) {

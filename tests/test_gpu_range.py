@@ -6,7 +6,7 @@ types): what the kernels do when an input leaves the range they compute in.
     Q' that overflowed), sets the status word: prefill_attn_status returns
     PA_EOVERFLOW.  Values inside the range leave it clear.
   * PA_IN_I16 splits each rotated Q'/K' value into int8 digits, exact for
-    values in [-8383, 8382].  A value outside sets PA_EOVERFLOW; the edge values
+    values in [-16448, 16319].  A value outside sets PA_EOVERFLOW; the edge values
     themselves are exact (scores bit-equal to the oracle).
 """
 
@@ -89,7 +89,7 @@ def _i16_case(x0, where="q"):
     return w, q, k, v
 
 
-@pytest.mark.parametrize("x0", [8382, -8383])
+@pytest.mark.parametrize("x0", [16319, -16448])
 @pytest.mark.parametrize("where", ["q", "k"])
 def test_int16_digit_range_edges_exact(x0, where):
     w, q, k, v = _i16_case(x0, where)
@@ -115,7 +115,7 @@ def test_int16_digit_range_edges_exact(x0, where):
     assert_close(o.cpu().numpy(), oracle_full(w, q, k, v), "bf16")
 
 
-@pytest.mark.parametrize("x0", [8383, -8384, 20000])
+@pytest.mark.parametrize("x0", [16320, -16449, 20000])
 @pytest.mark.parametrize("where", ["q", "k"])
 def test_int16_digit_range_exceeded_sets_status(x0, where):
     w, q, k, v = _i16_case(x0, where)
