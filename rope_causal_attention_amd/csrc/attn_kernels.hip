@@ -1036,23 +1036,22 @@ struct FusedAttn {
     typename P::Guard guard;  // range of this thread's converted Q' / K' values
     f32x16 o[D / 32];
     float m_run, l_a, l_b;
-    // kShift: the scores arrive shifted by b_run, subtracted by the Q.K^T
-    // products themselves (the C operand of the matrix-core path), so the
-    // softmax exponentiates them as they are instead of subtracting the
-    // running max from each.  b_run is 0 until the lane's first maximum is
-    // known, then m_run, which moves only when a tile's maximum passes it by
-    // more than the slack.  The shift rounds differently from a later
-    // subtraction, so it is chosen per score type, never per schedule or
-    // launch shape: every launch of one input type then gives the same bits
-    // (chunked, cached, packed and plain launches agree).  The integer paths
-    // subtract after their scaling FMA (their eight-wave kernels have no
-    // registers for it).  At head_dim 128 the 16 entries of -b_run stay in
-    // registers, which every fp16 schedule there has to spare; at 64 and 96
-    // they would spill (the paired eight-wave 96, the two-workgroup four-wave
-    // 64), so there the entries are written afresh before each product (a
-    // few register moves per 32-key block, against 32 subtractions per tile).
-    static constexpr bool kShift = !P::kIntScores;
-    static constexpr bool kKeepShift = kShift && D == 128;
+    // The scores arrive shifted by b_run, subtracted by the Q.K^T products
+    // themselves (the C operand of the fp16 matrix-core path, the scaling FMA
+    // of the integer ones), so the softmax exponentiates them as they are
+    // instead of subtracting the running max from each.  b_run is 0 until the
+    // lane's first maximum is known, then m_run, which moves only when a
+    // tile's maximum passes it by more than the slack.  The shift rounds
+    // differently from a later subtraction, and every launch shape of every
+    // input type takes it the same way, so chunked, cached, packed and plain
+    // launches give the same bits.  fp16 path: at head_dim 128 the 16 entries
+    // of -b_run stay in registers, which every schedule there has to spare;
+    // at 64 and 96 they would spill (the paired eight-wave 96, the
+    // two-workgroup four-wave 64), so there the entries are written afresh
+    // before each product (a few register moves per 32-key block, against 32
+    // subtractions per tile).  The integer paths use one entry, in the FMA.
+    static constexpr bool kShift = true;
+    static constexpr bool kKeepShift = D == 128 && !P::kIntScores;
     float b_run;
     f32x16 nbias;  // kKeepShift: -b_run in every entry
     __device__ __forceinline__ void set_shift(float b) {
