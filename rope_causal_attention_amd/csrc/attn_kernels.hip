@@ -638,8 +638,12 @@ struct I16QK {
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const uint32_t h = static_cast<uint32_t>(hh[v]), l = static_cast<uint32_t>(ll[v]);
-            s[v] = static_cast<int>((h << 14) + (static_cast<uint32_t>(x[v]) << 7) + l);
+            // ((hh 2^7 + x) 2^7 + ll, the same value mod 2^32, as two shift-adds;
+            // the empty asm (no instruction) keeps the compiler from spreading
+            // the shifts back over three instructions
+            uint32_t t = (static_cast<uint32_t>(hh[v]) << 7) + static_cast<uint32_t>(x[v]);
+            asm("" : "+v"(t));
+            s[v] = static_cast<int>((t << 7) + static_cast<uint32_t>(ll[v]));
         }
     }
 
