@@ -638,7 +638,7 @@ struct I16QK {
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            // ((hh 2^7 + x) 2^7 + ll, the same value mod 2^32, as two shift-adds;
+            // (hh 2^7 + x) 2^7 + ll, the same value mod 2^32, as two shift-adds;
             // the empty asm (no instruction) keeps the compiler from spreading
             // the shifts back over three instructions
             uint32_t t = (static_cast<uint32_t>(hh[v]) << 7) + static_cast<uint32_t>(x[v]);
